@@ -1,0 +1,378 @@
+"""Checks that pin the CPU oracle to the UniPrefill paper (arXiv 2605.06221).
+
+Each check takes the implementation under test as a namespace `impl` with the
+oracle's function names, so the same checks run against the oracle (they
+must pass) and against deliberately broken copies of it in
+test_oracle_mutations.py (each copy must fail at least one check).  None of
+the checks retypes the oracle's formula: they compare it with hand-worked
+fixtures, closed forms, brute force, library routines and invariants.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def bf16_bits(x):
+    """float -> bf16 bits by truncation-free RNE via float32 (test helper)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((b + (((b >> 16) & 1) + 0x7FFF)) >> 16).astype(np.uint16)
+
+
+def bits_to_f64(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Scores (Eq. 2-4)
+# ---------------------------------------------------------------------------
+def check_uniform_fixture(impl):
+    """Q = 0 hand example (N=8, n=2, G=4, one head)."""
+    g = load_golden("uniform_closed_form.json")
+    N, n, G = g["N"], g["n"], g["G"]
+    q = np.zeros((N, 1, 16), np.uint16)
+    k = bf16_bits(np.random.default_rng(0).standard_normal((N, 1, 16)))
+    b, o = impl.request_block_scores(q, k, 0, N, 1, 1, 16, G, n)
+    assert np.allclose(o * 56, g["importance_times_56"], rtol=0, atol=1e-12), o * 56
+    assert np.allclose(b * 112, g["block_scores_times_112"], rtol=0, atol=1e-12), b * 112
+
+
+def check_uniform_closed_form(impl):
+    """Q = 0 closed form on ragged shapes: o_i = Hq * sum_{j >= max(i, N-n_eff)} 1/(j+1)."""
+    rng = np.random.default_rng(1)
+    for (N, n, G, hq, hkv) in [(37, 5, 8, 4, 2), (5, 8, 4, 2, 1), (64, 16, 16, 3, 1), (1, 4, 4, 2, 2)]:
+        d = 8
+        q = np.zeros((N + 3, hq, d), np.uint16)
+        k = bf16_bits(rng.standard_normal((N + 3, hkv, d)))
+        b, o = impl.request_block_scores(q, k, 3, N, hq, hkv, d, G, n)
+        ne = min(n, N)
+        exp_o = np.array([hq * sum(Fraction(1, j + 1) for j in range(max(i, N - ne), N))
+                          for i in range(N)], dtype=object)
+        assert np.allclose(o, exp_o.astype(float), rtol=1e-12, atol=0), (N, n, o, exp_o)
+        nb = -(-N // G)
+        exp_b = [float(sum(exp_o[g * G: min(N, (g + 1) * G)]) / (G * ne)) for g in range(nb)]
+        assert np.allclose(b, exp_b, rtol=1e-12, atol=0), (N, n, G, b, exp_b)
+
+
+def _torch_reference_o(q, k, start, N, hq, hkv, d, n, scale):
+    import torch
+    ne = min(n, N)
+    o = torch.zeros(N, dtype=torch.float64)
+    for h in range(hq):
+        kv = h // (hq // hkv)
+        Q = torch.from_numpy(bits_to_f64(q[start + N - ne: start + N, h]))
+        K = torch.from_numpy(bits_to_f64(k[start: start + N, kv]))
+        for t in range(ne):
+            pos = N - ne + t
+            logits = (K[: pos + 1] @ Q[t]) * scale
+            o[: pos + 1] += torch.softmax(logits, dim=0)
+    return o.numpy()
+
+
+def check_vs_torch_softmax(impl):
+    """Random tiny shapes against torch.softmax (float64, CPU), row by row."""
+    rng = np.random.default_rng(2)
+    for (N, n, G, hq, hkv, d) in [(29, 6, 8, 4, 2, 16), (16, 16, 4, 2, 2, 8), (40, 7, 16, 6, 3, 32)]:
+        q = bf16_bits(rng.standard_normal((N + 5, hq, d)) * 1.5)
+        k = bf16_bits(rng.standard_normal((N + 5, hkv, d)) * 1.5)
+        scale = 1.0 / math.sqrt(d)
+        b, o = impl.request_block_scores(q, k, 2, N, hq, hkv, d, G, n)
+        ref = _torch_reference_o(q, k, 2, N, hq, hkv, d, n, scale)
+        assert np.allclose(o, ref, rtol=1e-12, atol=1e-14)
+        # explicit scale override
+        b2, o2 = impl.request_block_scores(q, k, 2, N, hq, hkv, d, G, n, scale=0.3)
+        ref2 = _torch_reference_o(q, k, 2, N, hq, hkv, d, n, 0.3)
+        assert np.allclose(o2, ref2, rtol=1e-12, atol=1e-14)
+
+
+def check_mass_invariant(impl):
+    """Every window row sums to one: sum_g b_g * G * n_eff = Hq * n_eff."""
+    rng = np.random.default_rng(3)
+    for (N, n, G, hq, hkv, d) in [(100, 8, 16, 8, 2, 16), (7, 16, 4, 2, 1, 8)]:
+        q = bf16_bits(rng.standard_normal((N, hq, d)) * 3)
+        k = bf16_bits(rng.standard_normal((N, hkv, d)) * 3)
+        b, _ = impl.request_block_scores(q, k, 0, N, hq, hkv, d, G, n)
+        ne = min(n, N)
+        assert abs(b.sum() * G * ne - hq * ne) < 1e-12 * hq * ne
+
+
+def check_gqa_invariance(impl):
+    """Replicating each KV head over its query group (so Hkv = Hq) changes nothing."""
+    rng = np.random.default_rng(4)
+    N, n, G, hq, hkv, d = 50, 9, 8, 8, 2, 16
+    q = bf16_bits(rng.standard_normal((N, hq, d)) * 2)
+    k = bf16_bits(rng.standard_normal((N, hkv, d)) * 2)
+    group = hq // hkv
+    k_full = np.repeat(k, group, axis=1)     # head h gets kv head h // group
+    b1, _ = impl.request_block_scores(q, k, 0, N, hq, hkv, d, G, n)
+    b2, _ = impl.request_block_scores(q, k_full, 0, N, hq, hq, d, G, n)
+    assert np.allclose(b1, b2, rtol=1e-13, atol=0)
+
+
+def check_spike(impl):
+    """One key with a +50 logit for every window row takes almost all mass."""
+    N, n, G, hq, d = 64, 8, 8, 2, 16
+    q = np.zeros((N, hq, d), np.float64)
+    q[:, :, 0] = 1.0
+    k = np.zeros((N, 1, d), np.float64)
+    k[19, 0, 0] = 50.0 * math.sqrt(d)
+    b, o = impl.request_block_scores(bf16_bits(q), bf16_bits(k), 0, N, hq, 1, d, G, n)
+    assert b[19 // G] * G * n > 0.999999 * hq * n
+    assert o[19] > 0.999999 * hq * n
+
+
+def check_packing_independence(impl):
+    """Blocks are anchored at each request's start: a packed batch scores each
+    request exactly as alone."""
+    rng = np.random.default_rng(5)
+    hq, hkv, d, G, n = 4, 2, 16, 8, 6
+    lens = [13, 1, 30, 8]
+    T = sum(lens)
+    q = bf16_bits(rng.standard_normal((T, hq, d)) * 2)
+    k = bf16_bits(rng.standard_normal((T, hkv, d)) * 2)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    b, offs = impl.block_scores(q, k, cu, hq, hkv, d, G, n)
+    for r, N in enumerate(lens):
+        s = cu[r]
+        br, _ = impl.request_block_scores(q[s: s + N].copy(), k[s: s + N].copy(), 0, N, hq, hkv, d, G, n)
+        assert np.array_equal(b[offs[r]: offs[r + 1]], br)
+        assert offs[r + 1] - offs[r] == -(-N // G)
+
+
+def check_causal(impl):
+    """A key after a window row's own position gets none of that row's mass."""
+    N, n, G, d = 16, 4, 4, 8
+    q = np.zeros((N, 1, d))
+    q[:, 0, 0] = 1.0
+    k = np.zeros((N, 1, d))
+    k[N - 1, 0, 0] = 30.0 * math.sqrt(d)      # huge logit on the very last key
+    b, o = impl.request_block_scores(bf16_bits(q), bf16_bits(k), 0, N, 1, 1, d, G, n)
+    # only the last window row can see key N-1; the other rows spread uniformly
+    rows = [N - n + t for t in range(n)]
+    exp_o0 = sum(1.0 / (j + 1) for j in rows[:-1])
+    assert abs(o[0] - exp_o0) < 1e-9, (o[0], exp_o0)
+    assert abs(o[N - 1] - 1.0) < 1e-9
+
+
+SCORE_CHECKS = [check_uniform_fixture, check_uniform_closed_form, check_vs_torch_softmax,
+                check_mass_invariant, check_gqa_invariance, check_spike,
+                check_packing_independence, check_causal]
+
+
+# ---------------------------------------------------------------------------
+# Top-p (Eq. 5, Eq. 14) and expansion
+# ---------------------------------------------------------------------------
+def check_topp_fixture(impl):
+    g = load_golden("topp_hand_example.json")
+    b = np.array(g["scores_times_64"], dtype=np.float32) / 64
+    keep = impl.top_p_select(b, g["p"])
+    assert sorted(np.nonzero(keep)[0].tolist()) == g["kept_blocks"]
+    order = np.argsort(impl.pack_keys(b))[::-1]
+    assert order.tolist() == g["descending_order"]
+
+
+def _brute_min_card(b, p):
+    """Smallest number of blocks whose exact mass reaches p times the total."""
+    fr = [Fraction(float(x)) for x in b]
+    tot = sum(fr)
+    pf = Fraction(p)
+    for size in range(1, len(b) + 1):
+        best = sum(sorted(fr, reverse=True)[:size])
+        if best >= pf * tot:
+            return size
+    return len(b)
+
+
+def check_topp_bruteforce(impl):
+    """|S| equals the minimum cardinality over all subsets (nb <= 9), and S is
+    the top-|S| prefix in packed-key order."""
+    rng = np.random.default_rng(6)
+    for trial in range(300):
+        nb = int(rng.integers(1, 10))
+        b = (rng.random(nb) ** 3).astype(np.float32)
+        p = float(rng.choice([0.5, 0.8, 0.9, 0.95, 0.99]))
+        keep = impl.top_p_select(b, p)
+        kmin = _brute_min_card(b, p)
+        assert keep.sum() == kmin, (b, p, keep, kmin)
+        # the minimal set is a prefix of the descending packed order
+        order = np.argsort(impl.pack_keys(b))[::-1]
+        assert set(np.nonzero(keep)[0]) == set(order[: kmin].tolist())
+        # exhaustive: no smaller subset of any kind reaches p (tiny nb only)
+        if nb <= 6 and kmin > 1:
+            fr = [Fraction(float(x)) for x in b]
+            tot = sum(fr)
+            for sub in itertools.combinations(range(nb), kmin - 1):
+                assert sum(fr[i] for i in sub) < Fraction(p) * tot
+
+
+def check_eq6_and_minimality(impl):
+    """Dropped mass <= (1-p) of the total (Eq. 6, aggregated form), and
+    removing the last kept block falls short of p."""
+    rng = np.random.default_rng(7)
+    for trial in range(200):
+        nb = int(rng.integers(2, 300))
+        b = np.exp(rng.standard_normal(nb) * 3).astype(np.float32)
+        p = float(rng.uniform(0.5, 0.999))
+        keep = impl.top_p_select(b, p)
+        bf = b.astype(np.float64)
+        tot = bf.sum()
+        slack = nb * 2.0 ** -50 * bf.max()
+        assert bf[~keep].sum() <= (1 - p) * tot + slack
+        kept_sorted = np.sort(bf[keep])
+        assert bf[keep].sum() - kept_sorted[0] < p * tot + slack
+
+
+def check_phi(impl):
+    """phi is strictly monotone over float32 (incl. +-0, subnormals, +-inf) and
+    packing round-trips."""
+    rng = np.random.default_rng(8)
+    special = np.array([-np.inf, -3.4e38, -1.0, -1e-40, -0.0, 0.0, 1e-45, 1e-40, 1.0, 3.4e38, np.inf],
+                       dtype=np.float32)
+    x = np.concatenate([special, (rng.standard_normal(2000) * 10.0 ** rng.integers(-40, 38, 2000)).astype(np.float32)])
+    ph = impl.phi(x).astype(np.int64)
+    xf = x.astype(np.float64)
+    order = np.lexsort((np.signbit(x).astype(int) * -1, xf))   # by value, -0 before +0
+    ph_sorted = ph[order]
+    assert np.all(np.diff(ph_sorted) >= 0)
+    assert impl.phi(np.array([-0.0], np.float32))[0] < impl.phi(np.array([0.0], np.float32))[0]
+    keys = impl.pack_keys(x)
+    assert np.array_equal((keys >> np.uint64(32)).astype(np.uint32), impl.phi(x))
+    assert np.array_equal((keys & np.uint64(0xFFFFFFFF)).astype(np.int64), np.arange(len(x)))
+
+
+def check_topp_edges(impl):
+    """p = 1 keeps every positive block and drops zero ones; an all-zero vector
+    keeps one block (k* >= 1); larger p never keeps fewer blocks."""
+    b = np.array([0.0, 2.0, 0.0, 1.0, 3.0], np.float32)
+    assert np.nonzero(impl.top_p_select(b, 1.0))[0].tolist() == [1, 3, 4]
+    z = np.zeros(5, np.float32)
+    assert np.nonzero(impl.top_p_select(z, 0.99))[0].tolist() == [4]
+    rng = np.random.default_rng(9)
+    for _ in range(50):
+        b = np.exp(rng.standard_normal(64) * 2).astype(np.float32)
+        prev = None
+        for p in [0.3, 0.6, 0.9, 0.99, 1.0]:
+            k = impl.top_p_select(b, p)
+            if prev is not None:
+                assert np.all(k >= prev)
+            prev = k
+
+
+def check_expand_fixture(impl):
+    g = load_golden("expand_hand_example.json")
+    b = np.array(g["scores_times_64"], dtype=np.float32) / 64
+    kb = impl.top_p_select(b, g["p"])
+    m = impl.expand_mask(kb, g["N"], g["G"], g["A"], g["n"])
+    assert m.tolist() == g["mask"]
+    assert int(m.sum()) == g["kept_tokens"]
+
+
+def check_expand_invariants(impl):
+    rng = np.random.default_rng(10)
+    for _ in range(100):
+        N = int(rng.integers(1, 300))
+        G = int(rng.integers(1, 40))
+        A = int(rng.integers(0, 50))
+        n = int(rng.integers(1, 50))
+        nb = -(-N // G)
+        kb = rng.random(nb) < 0.3
+        m = impl.expand_mask(kb, N, G, A, n)
+        i = np.arange(N)
+        assert np.all(m[i < A] == 1) and np.all(m[i >= N - n] == 1)
+        free = (i >= A) & (i < N - n)
+        assert np.array_equal(m[free].astype(bool), kb[i[free] // G])
+
+
+TOPP_CHECKS = [check_topp_fixture, check_topp_bruteforce, check_eq6_and_minimality,
+               check_phi, check_topp_edges, check_expand_fixture, check_expand_invariants]
+
+
+# ---------------------------------------------------------------------------
+# Compaction, carry-forward (Eq. 7-8) and metadata (Eq. 17)
+# ---------------------------------------------------------------------------
+def check_compact_roundtrip(impl):
+    """compact then scatter-back with identity sublayers returns the input
+    exactly; with f(x) = x + 1 exactly the kept rows change."""
+    rng = np.random.default_rng(11)
+    for _ in range(30):
+        lens = rng.integers(0, 50, size=int(rng.integers(1, 6)))
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        T = int(cu[-1])
+        mask = (rng.random(T) < 0.4).astype(np.uint8)
+        H = rng.integers(0, 2 ** 31, size=(T, 5), dtype=np.int64)
+        (out,), idx, cu_out = impl.compact(mask, cu, [H])
+        assert np.array_equal(out, H[mask.astype(bool)])
+        assert np.all(np.diff(idx) > 0)
+        assert cu_out[-1] == mask.sum() and np.all(np.diff(cu_out) >= 0)
+        for r in range(len(lens)):
+            assert cu_out[r + 1] - cu_out[r] == mask[cu[r]: cu[r + 1]].sum()
+        back = impl.scatter_back(H, out, idx, len(idx))
+        assert np.array_equal(back, H)
+        back2 = impl.scatter_back(H, out + 1, idx, len(idx))
+        changed = np.any(back2 != H, axis=1)
+        assert np.array_equal(changed, mask.astype(bool))
+
+
+def check_compact_composition(impl):
+    """A second drop on the compacted stream maps back through the first
+    index map to the original rows."""
+    rng = np.random.default_rng(12)
+    lens = [40, 25, 33]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    H = np.arange(T * 3).reshape(T, 3)
+    m1 = (rng.random(T) < 0.6).astype(np.uint8)
+    (h1,), i1, cu1 = impl.compact(m1, cu, [H])
+    m2 = (rng.random(int(cu1[-1])) < 0.5).astype(np.uint8)
+    (h2,), i2, cu2 = impl.compact(m2, cu1, [h1], index_in=i1)
+    assert np.array_equal(H[i2], h2)
+    keep_both = np.zeros(T, bool)
+    keep_both[np.nonzero(m1)[0][m2.astype(bool)]] = True
+    assert np.array_equal(i2, np.nonzero(keep_both)[0])
+
+
+def check_eq17_fixture(impl):
+    g = load_golden("eq17_example.json")
+    st = impl.MetadataState.fresh([g["orig_len"]])
+    cu_old = np.array([0, g["orig_len"]])
+    for layer, kept in g["drops"]:
+        cu_new = np.array([0, kept])
+        st, nat = impl.update_metadata(st, layer, cu_old, cu_new)
+        assert nat == kept
+        cu_old = cu_new
+    for lp, want in g["seqused_by_layer"].items():
+        got = impl.seqused_eq17(st.history[0], int(lp), g["orig_len"], g["kv_len"])
+        assert got == want, (lp, got, want)
+
+
+def check_metadata_conservation(impl):
+    """seq_lens drop by exactly the dropped count; prior context is kept."""
+    rng = np.random.default_rng(13)
+    lens = rng.integers(1, 100, size=6)
+    ctx = rng.integers(0, 50, size=6)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    kept = np.array([int(rng.integers(0, L + 1)) for L in lens])
+    cu_new = np.concatenate([[0], np.cumsum(kept)])
+    st = impl.MetadataState.fresh(lens + ctx)
+    st2, nat = impl.update_metadata(st, 3, cu, cu_new)
+    assert np.array_equal(st2.seq_lens, ctx + kept)
+    assert nat == kept.sum()
+    assert all(h == [(3, int(ctx[r] + kept[r]))] for r, h in enumerate(st2.history))
+
+
+COMPACT_CHECKS = [check_compact_roundtrip, check_compact_composition,
+                  check_eq17_fixture, check_metadata_conservation]
+
+ALL_CHECKS = SCORE_CHECKS + TOPP_CHECKS + COMPACT_CHECKS

@@ -1,0 +1,210 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins
+catch every one of them.  This shows the pins are strong enough to tie the
+oracle to the paper: a dropped term, a wrong sign or index, or a transposed
+operand anywhere in it fails at least one check.  Everything runs on the CPU;
+the oracle itself is never modified."""
+from __future__ import annotations
+
+import math
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+import pins
+from oracle import uniprefill_oracle as U
+
+
+def _namespace(**over):
+    ns = types.SimpleNamespace(**{name: getattr(U, name) for name in dir(U) if not name.startswith("_")})
+    for k, v in over.items():
+        setattr(ns, k, v)
+    return ns
+
+
+def _importance_variant(head_mean=False, causal=True, gqa="floor", scale_one=False, transpose_rows=False):
+    def token_importance(q_bits, k_bits, start, N, hq, hkv, d, n, scale=None):
+        if N <= 0:
+            return np.zeros(0)
+        ne = min(n, N)
+        sc = 1.0 if scale_one else (1.0 / math.sqrt(d) if (scale is None or scale <= 0) else float(scale))
+        keys = np.arange(N)
+        rowpos = (N - ne) + np.arange(ne)
+        if transpose_rows:
+            rowpos = rowpos[::-1]
+        future = keys[None, :] > rowpos[:, None]
+        o = np.zeros(N)
+        for h in range(hq):
+            kv = (h * hkv) // hq if gqa == "floor" else h % hkv
+            Qw = U.bf16_bits_to_f64(q_bits[start + N - ne: start + N, h, :])
+            Kr = U.bf16_bits_to_f64(k_bits[start: start + N, kv, :])
+            Z = (Qw @ Kr.T) * sc
+            if causal:
+                Z[future] = -np.inf
+            Z -= Z.max(axis=1, keepdims=True)
+            E = np.exp(Z)
+            o += (E / E.sum(axis=1, keepdims=True)).sum(axis=0)
+        return o / hq if head_mean else o
+    return token_importance
+
+
+def _scores_variant(ti, partial_true_len=False, use_n=False):
+    def request_block_scores(q_bits, k_bits, start, N, hq, hkv, d, G, n, scale=None):
+        o = ti(q_bits, k_bits, start, N, hq, hkv, d, n, scale)
+        if N <= 0:
+            return np.zeros(0), o
+        ne = n if use_n else min(n, N)
+        nb = -(-N // G)
+        b = np.zeros(nb)
+        for g in range(nb):
+            seg = o[g * G: min((g + 1) * G, N)]
+            b[g] = seg.sum() / ((len(seg) if partial_true_len else G) * ne)
+        return b, o
+
+    def block_scores(q_bits, k_bits, cu_seqlens, hq, hkv, d, G, n, scale=None):
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        parts, offs = [], [0]
+        for r in range(len(cu) - 1):
+            b, _ = request_block_scores(q_bits, k_bits, int(cu[r]), int(cu[r + 1] - cu[r]), hq, hkv, d, G, n, scale)
+            parts.append(b)
+            offs.append(offs[-1] + len(b))
+        return np.concatenate(parts), np.asarray(offs)
+    return request_block_scores, block_scores
+
+
+def _scoring_mutant(ti_kw=None, **sc_kw):
+    ti = _importance_variant(**(ti_kw or {}))
+    rbs, bs = _scores_variant(ti, **sc_kw)
+    return _namespace(token_importance=ti, request_block_scores=rbs, block_scores=bs)
+
+
+def _topp_variant(tie="larger_first", exclusive=False, ascending=False, float_sum=False):
+    def pack_keys(b32):
+        g = np.arange(len(b32), dtype=np.uint64)
+        if tie == "smaller_first":
+            g = np.uint64(len(b32) - 1) - g if len(b32) else g
+        return (U.phi(b32).astype(np.uint64) << np.uint64(32)) | g
+
+    def top_p_select(b32, p):
+        b32 = np.ascontiguousarray(b32, dtype=np.float32)
+        nb = len(b32)
+        keep = np.zeros(nb, bool)
+        if nb == 0:
+            return keep
+        order = np.argsort(pack_keys(b32), kind="stable")
+        if not ascending:
+            order = order[::-1]
+        bf = b32.astype(np.float64)
+        if float_sum:          # mass taken as the count of blocks, not their scores
+            cs = np.cumsum(np.ones(nb))
+            thr = p * nb
+        else:
+            cs = np.cumsum(bf[order])
+            thr = p * bf.sum()
+        hit = np.nonzero(cs >= thr)[0]
+        kstar = int(hit[0]) + 1 if len(hit) else nb
+        if exclusive:
+            kstar -= 1
+        keep[order[:kstar]] = True
+        return keep
+    return _namespace(pack_keys=pack_keys, top_p_select=top_p_select)
+
+
+def _phi_ge_zero(b32):
+    x = np.ascontiguousarray(b32, dtype=np.float32)
+    bits = x.view(np.uint32)
+    return np.where(x >= 0, bits ^ np.uint32(0x80000000), bits ^ np.uint32(0xFFFFFFFF)).astype(np.uint32)
+
+
+def _expand_no_window(keep_block, N, G, A, n):
+    i = np.arange(N)
+    return (keep_block[i // G] | (i < A)).astype(np.uint8)
+
+
+def _expand_off_by_one(keep_block, N, G, A, n):
+    i = np.arange(N)
+    return (keep_block[i // G] | (i <= A) | (i > N - n)).astype(np.uint8)
+
+
+def _compact_no_compose(mask, cu_seqlens, buffers=(), index_in=None):
+    return U.compact(mask, cu_seqlens, buffers, None)
+
+
+def _compact_cu_inclusive(mask, cu_seqlens, buffers=(), index_in=None):
+    outs, idx, cu_out = U.compact(mask, cu_seqlens, buffers, index_in)
+    cu = np.asarray(cu_seqlens)
+    m = np.asarray(mask).astype(np.int64)
+    cu_out = np.array([m[: min(c + 1, len(m))].sum() for c in cu], dtype=np.int32)
+    return outs, idx, cu_out
+
+
+def _seqused_le(history_r, layer_prime, orig_len, kv_len):
+    before = [(l, s) for (l, s) in history_r if l <= layer_prime]
+    base = max(before)[1] if before else orig_len
+    return int(base + (kv_len - orig_len))
+
+
+def _seqused_first(history_r, layer_prime, orig_len, kv_len):
+    before = [(l, s) for (l, s) in history_r if l < layer_prime]
+    base = min(before)[1] if before else orig_len
+    return int(base + (kv_len - orig_len))
+
+
+def _update_sets_kept(state, layer, cu_old, cu_new):
+    cu_new = np.asarray(cu_new)
+    seq = np.diff(cu_new).astype(np.int64)
+    hist = [list(h) + [(int(layer), int(seq[r]))] for r, h in enumerate(state.history)]
+    return U.MetadataState(seq, hist), int(cu_new[-1])
+
+
+def _scatter_all(full, compacted, index_map, count):
+    out = np.array(full, copy=True)
+    n = min(len(out), len(compacted))
+    out[:n] = np.asarray(compacted)[:n]
+    return out
+
+
+MUTANTS = {
+    "head_mean": _scoring_mutant(ti_kw=dict(head_mean=True)),
+    "no_causal_mask": _scoring_mutant(ti_kw=dict(causal=False)),
+    "gqa_modulo": _scoring_mutant(ti_kw=dict(gqa="mod")),
+    "scale_missing": _scoring_mutant(ti_kw=dict(scale_one=True)),
+    "window_rows_reversed": _scoring_mutant(ti_kw=dict(transpose_rows=True)),
+    "partial_block_true_len": _scoring_mutant(partial_true_len=True),
+    "n_instead_of_n_eff": _scoring_mutant(use_n=True),
+    "tie_smaller_index_first": _topp_variant(tie="smaller_first"),
+    "kstar_exclusive": _topp_variant(exclusive=True),
+    "ascending_sort": _topp_variant(ascending=True),
+    "count_not_mass": _topp_variant(float_sum=True),
+    "phi_by_value": _namespace(phi=_phi_ge_zero),
+    "expand_no_window": _namespace(expand_mask=_expand_no_window),
+    "expand_off_by_one": _namespace(expand_mask=_expand_off_by_one),
+    "compact_no_compose": _namespace(compact=_compact_no_compose),
+    "cu_out_inclusive": _namespace(compact=_compact_cu_inclusive),
+    "scatter_everything": _namespace(scatter_back=_scatter_all),
+    "eq17_le": _namespace(seqused_eq17=_seqused_le),
+    "eq17_first_drop": _namespace(seqused_eq17=_seqused_first),
+    "seq_lens_set_to_kept": _namespace(update_metadata=_update_sets_kept),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    impl = MUTANTS[name]
+    failures = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(impl)
+        except AssertionError:
+            failures.append(check.__name__)
+        except Exception as e:  # a crash is also a catch, but say which
+            failures.append(f"{check.__name__}:{type(e).__name__}")
+    assert failures, f"mutant {name} passed every pin"
+
+
+def test_unmutated_namespace_passes():
+    impl = _namespace()
+    for check in pins.ALL_CHECKS:
+        check(impl)
+    assert impl.top_p_select is oracle.top_p_select
