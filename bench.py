@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the UniPrefill token-selection hot path on one MI355X.
+
+One step = one full-attention layer's pass over the hot path on the resident
+workload: up_select_blocks (score GEMM + online softmax + block reduce, top-p,
+expansion), up_compact of the hidden rows, up_update_metadata, and the Eq. 8
+up_scatter_back.  The workload is one 131072-token request shaped like a
+LLaMA-3.1-8B full-attention layer (32 query heads, 8 KV heads, head_dim 128,
+hidden 4096, bf16), seeded synthetic data (synth.llama_128k).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+METRIC = "selected+compacted prefill tokens/s at 128K (1 GPU); % MFMA and % HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime's C API (the library records
+    them on the stream its kernels run on)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def new(self):
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.events.append(e.value)
+        return e.value
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        self.hip.hipEventSynchronize(b)
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
+def cpu_oracle_step(wl, cu, q, k, hidden_host):
+    """One step of the same path through the CPU oracle (float64 NumPy)."""
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    sel = oracle.select(q, k, cu, wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p)
+    (out,), idx, cu_out = oracle.compact(sel["mask"], cu, [hidden_host])
+    st = oracle.MetadataState.fresh(np.diff(cu))
+    st, nat = oracle.update_metadata(st, 0, cu, cu_out)
+    full = oracle.scatter_back(hidden_host, out, idx, len(idx))
+    dt = time.perf_counter() - t0
+    del full, out
+    return dt, sel
+
+
+def threads_used():
+    n = len(os.sched_getaffinity(0))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
+        v = os.environ.get(var)
+        if v and v.isdigit():
+            n = min(n, int(v))
+    return n
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures the single-GPU hot path only; --gpus {args.gpus} is not supported "
+              "(nothing in this path spans GPUs).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import token_level_block_amd as tlb
+    from token_level_block_amd.runner import CompactBuffers, MetadataBuffers, SelectBuffers, run_scatter_back
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    wl = synth.llama_128k()
+    log(f"[bench] generating {wl.name}: lengths={wl.lengths} hq={wl.hq} hkv={wl.hkv} d={wl.d} D={wl.hidden}")
+    cu, q, k = synth.make_qk(wl)
+    T = int(cu[-1])
+    R = wl.num_reqs
+    nwords = wl.hidden // 2
+    cu_d = torch.from_numpy(cu).cuda()
+    qd = torch.zeros((T, wl.hq, wl.d), dtype=torch.int16, device="cuda")
+    for r in range(R):
+        s, N = int(cu[r]), int(cu[r + 1] - cu[r])
+        ne = min(wl.n, N)
+        qd[s + N - ne: s + N] = torch.from_numpy(q[s + N - ne: s + N].view(np.int16)).cuda()
+    kd = torch.from_numpy(k.view(np.int16)).cuda()
+    hidden = synth.hidden_words_torch(0, T, nwords, "cuda")
+    out = torch.empty_like(hidden)
+    full = hidden.clone()
+
+    prm = tlb.make_params(wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p)
+    sel = SelectBuffers.allocate(prm, R, T)
+    cb = CompactBuffers.allocate(R, T)
+    mb = MetadataBuffers.allocate(np.diff(cu), num_layers=32, max_drops=4)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents()
+
+    def step(marks=None):
+        if marks is not None:
+            prm.prof_score_begin, prm.prof_score_end = marks["score"]
+            ev.record(marks["t0"], stream)
+        else:
+            prm.prof_score_begin = prm.prof_score_end = None
+        sel.run(qd, kd, cu_d, stream=stream)
+        if marks is not None:
+            ev.record(marks["t1"], stream)
+        cb.run(sel.keep_mask, cu_d, [hidden], [out], stream=stream)
+        if marks is not None:
+            ev.record(marks["t2"], stream)
+        mb.run(0, cu_d, cb.cu_out, stream=stream)
+        if marks is not None:
+            ev.record(marks["t3"], stream)
+        run_scatter_back(out, cb.index_out, cb.cu_out, R, T, full, stream=stream)
+        if marks is not None:
+            ev.record(marks["t4"], stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [dict(score=(ev.new(), ev.new()), t0=ev.new(), t1=ev.new(), t2=ev.new(), t3=ev.new(), t4=ev.new())
+             for _ in range(args.steps)]
+    start, stop = ev.new(), ev.new()
+    torch.cuda.synchronize()
+    ev.record(start, stream)
+    for i in range(args.steps):
+        step(marks[i])
+    ev.record(stop, stream)
+    torch.cuda.synchronize()
+    total_ms = ev.ms(start, stop)
+    ms_per_step = total_ms / args.steps
+    def mean(a, b):
+        return sum(ev.ms(m[a], m[b]) for m in marks) / len(marks)
+
+    score_ms = sum(ev.ms(*m["score"]) for m in marks) / len(marks)
+    select_ms = mean("t0", "t1")
+    compact_ms = mean("t1", "t2")
+    meta_ms = mean("t2", "t3")
+    scatter_ms = mean("t3", "t4")
+
+    kept = int(sel.kept[:R].sum().item())
+    keep_ratio = kept / T
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    sel_compact_tps = T / ((select_ms + compact_ms + meta_ms) * 1e-3)
+
+    flops = 2.0 * wl.n * wl.hq * wl.d * T
+    score_tflops = flops / (score_ms * 1e-3) / 1e12
+    row_bytes = wl.hidden * 2
+    compact_bytes = 2 * kept * row_bytes + 4 * kept + T
+    compact_gbs = compact_bytes / (compact_ms * 1e-3) / 1e9
+    scatter_bytes = 2 * kept * row_bytes + 4 * kept
+    scatter_gbs = scatter_bytes / (scatter_ms * 1e-3) / 1e9
+    log(f"[bench] {ms_per_step:.3f} ms/step  select {select_ms:.3f} (score {score_ms:.3f}) compact "
+        f"{compact_ms:.3f} metadata {meta_ms:.3f} scatter {scatter_ms:.3f}  kept {kept}/{T}")
+    ev.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on one full step of the same workload")
+        hidden_host = synth.hidden_words(np.arange(T), nwords)
+        dt, _ = cpu_oracle_step(wl, cu, q, k, hidden_host)
+        cpu = {"value": T / dt, "unit": "tokens/s", "cores": threads_used(), "kind": "oracle",
+               "sample": f"one full step (select, compact, metadata, scatter-back) of the {T}-token request, "
+                         f"{dt:.1f} s wall"}
+        log(f"[bench] oracle step {dt:.2f} s -> {T / dt:.0f} tokens/s")
+
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "requests": R, "tokens": T, "num_heads_q": wl.hq,
+                   "num_heads_kv": wl.hkv, "head_dim": wl.d, "hidden": wl.hidden, "G": wl.G, "A": wl.A,
+                   "n": wl.n, "p": wl.p, "keep_ratio": round(keep_ratio, 4)},
+        "roofline": {"bound": "mfma", "kernel": "score_kernel<128>", "achieved": score_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": score_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None},
+        "roofline_compact": {"bound": "hbm", "kernel": "up_compact", "achieved": compact_gbs,
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": compact_gbs / PEAK_HBM_GBS},
+        "roofline_scatter": {"bound": "hbm", "kernel": "up_scatter_back", "achieved": scatter_gbs,
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": scatter_gbs / PEAK_HBM_GBS},
+        "breakdown_ms": {"select": select_ms, "score_kernel": score_ms, "compact": compact_ms,
+                         "metadata": meta_ms, "scatter_back": scatter_ms},
+        "select_compact_tokens_per_s": sel_compact_tps,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

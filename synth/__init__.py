@@ -50,7 +50,7 @@ STRUCT_BLOCK = 64    # granularity of the generator's hot/cold structure
 
 # Calibrated generator constants (see tests/golden/calibrate_generator.py,
 # which bisects them against the oracle's keep ratio at p = 0.99).
-POWERLAW_C = 1.0     # replaced below by the calibrated value
+POWERLAW_C = 1.4590  # keeps 40.1% of the 2048 blocks of the 128K request at p = 0.99
 HOT_LAMBDA_VARLEN = 8.0
 
 LLAMA_8B = dict(hq=32, hkv=8, d=128, hidden=4096)

@@ -1,0 +1,168 @@
+"""The C ABI library on the CPU: it loads, exports every symbol the header
+declares, sizes workspaces, and rejects bad arguments on the host before any
+launch (every call below fails validation, so no HIP work is attempted)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+tlb = pytest.importorskip("token_level_block_amd")
+
+HEADER = os.path.join(ROOT, "include", "uniprefill.h")
+FAKE = 1 << 20            # a nonzero, 256-aligned address that is never dereferenced
+FAKE_MIS = FAKE + 2       # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(up_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 8
+    lib = ctypes.CDLL(tlb.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(tlb.EXPORTED)
+
+
+def test_status_strings():
+    for code in range(0, -7, -1):
+        assert tlb.status_string(code) and tlb.status_string(code) != "unknown status"
+    assert tlb.status_string(-99) == "unknown status"
+
+
+def p(**kw):
+    base = dict(num_heads_q=32, num_heads_kv=8, head_dim=128, block_size=64, num_sink=128, window=128,
+                top_p=0.99)
+    base.update(kw)
+    scores_in = base.pop("scores_in", False)
+    return tlb.make_params(**base, scores_in=scores_in)
+
+
+def test_max_blocks_bound():
+    assert tlb.max_blocks(64, 1, 131072) == 2048 + 1
+    assert tlb.max_blocks(64, 4, 30720) == 480 + 4
+    assert tlb.max_blocks(0, 1, 10) == -1
+    # the bound covers any split of max_tokens into num_reqs requests
+    for lens in ([1] * 7, [64, 64, 1], [63, 1, 127], [4096, 8192, 16384, 2048]):
+        T, R = sum(lens), len(lens)
+        assert sum(math.ceil(L / 64) for L in lens) <= tlb.max_blocks(64, R, T)
+
+
+def test_workspace_sizes():
+    prm = p()
+    ws = tlb.select_workspace_bytes(prm, 1, 131072)
+    rows = 32 * 128
+    # block partials + chunk partials dominate
+    assert ws >= 4 * rows * (2048 + 1)
+    assert ws % 256 == 0
+    assert tlb.select_workspace_bytes(p(scores_in=True), 1, 131072) < 64 * 1024
+    assert tlb.select_workspace_bytes(p(head_dim=96), 1, 100) == 0
+    assert tlb.compact_workspace_bytes(4, 30720) > 0
+    assert tlb.compact_workspace_bytes(-1, 10) == 0
+
+
+def call_select(prm, q=FAKE, qs=32 * 128, k=FAKE, ks=8 * 128, cu=FAKE, R=1, T=4096, scores=None,
+                mask=FAKE, kept=FAKE, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = tlb.select_workspace_bytes(prm, R, T) if tlb.select_workspace_bytes(prm, R, T) else 1 << 40
+    return tlb.select_blocks(prm, q, qs, k, ks, cu, R, T, scores, None, None, None, mask, kept, ws,
+                             workspace_bytes=wsb, stream=0, raise_on_error=False)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_heads_kv=5), tlb.UP_ERR_SHAPE),
+    (dict(num_heads_q=0), tlb.UP_ERR_SHAPE),
+    (dict(head_dim=96), tlb.UP_ERR_PARAM),
+    (dict(block_size=48), tlb.UP_ERR_PARAM),
+    (dict(block_size=0), tlb.UP_ERR_PARAM),
+    (dict(window=0), tlb.UP_ERR_PARAM),
+    (dict(num_sink=-1), tlb.UP_ERR_PARAM),
+    (dict(top_p=0.0), tlb.UP_ERR_PARAM),
+    (dict(top_p=1.5), tlb.UP_ERR_PARAM),
+    (dict(top_p=float("nan")), tlb.UP_ERR_PARAM),
+    (dict(softmax_scale=float("inf")), tlb.UP_ERR_PARAM),
+])
+def test_select_rejects_params(kw, code):
+    assert call_select(p(**kw)) == code
+
+
+def test_select_rejects_nulls_shapes_alignment_workspace():
+    prm = p()
+    assert tlb.select_blocks(None, FAKE, 1, FAKE, 1, FAKE, 1, 1, None, None, None, None, FAKE, FAKE,
+                             FAKE, workspace_bytes=1 << 30, stream=0, raise_on_error=False) == tlb.UP_ERR_NULL
+    assert call_select(prm, q=None) == tlb.UP_ERR_NULL
+    assert call_select(prm, cu=None) == tlb.UP_ERR_NULL
+    assert call_select(prm, mask=None) == tlb.UP_ERR_NULL
+    assert call_select(prm, kept=None) == tlb.UP_ERR_NULL
+    assert call_select(prm, ws=None) == tlb.UP_ERR_NULL
+    assert call_select(p(scores_in=True), q=None, k=None, scores=None) == tlb.UP_ERR_NULL
+    assert call_select(prm, R=-1) == tlb.UP_ERR_SHAPE
+    assert call_select(prm, T=-5) == tlb.UP_ERR_SHAPE
+    assert call_select(prm, T=2 ** 31) == tlb.UP_ERR_SHAPE
+    assert call_select(prm, qs=100) == tlb.UP_ERR_SHAPE          # smaller than Hq*d
+    assert call_select(prm, q=FAKE_MIS) == tlb.UP_ERR_ALIGN
+    assert call_select(prm, ks=8 * 128 + 4) == tlb.UP_ERR_ALIGN
+    assert call_select(prm, ws=FAKE + 16) == tlb.UP_ERR_ALIGN
+    need = tlb.select_workspace_bytes(prm, 1, 4096)
+    assert call_select(prm, wsb=need - 1) == tlb.UP_ERR_WORKSPACE
+
+
+def test_scores_in_mode_accepts_any_block_size_in_planning():
+    prm = p(scores_in=True, block_size=7, head_dim=1)
+    assert tlb.select_workspace_bytes(prm, 3, 1000) > 0
+    # still rejects a too-small workspace before launching
+    assert call_select(prm, q=None, k=None, scores=FAKE, wsb=16) == tlb.UP_ERR_WORKSPACE
+
+
+def call_compact(mask=FAKE, cu=FAKE, R=2, T=1000, src=(FAKE,), dst=(FAKE,), rb=(8192,), iout=FAKE,
+                 cuo=FAKE, ws=FAKE, wsb=1 << 30):
+    return tlb.compact(mask, cu, R, T, list(src), list(dst), list(rb), None, iout, cuo, ws,
+                       workspace_bytes=wsb, stream=0, raise_on_error=False)
+
+
+def test_compact_rejects():
+    assert call_compact(mask=None) == tlb.UP_ERR_NULL
+    assert call_compact(iout=None) == tlb.UP_ERR_NULL
+    assert call_compact(src=(None,)) == tlb.UP_ERR_NULL
+    assert call_compact(R=-1) == tlb.UP_ERR_SHAPE
+    assert call_compact(rb=(6,)) == tlb.UP_ERR_PARAM
+    assert call_compact(rb=(0,)) == tlb.UP_ERR_PARAM
+    assert call_compact(src=(FAKE,) * 9, dst=(FAKE,) * 9, rb=(16,) * 9) == tlb.UP_ERR_PARAM
+    assert call_compact(mask=FAKE + 1) == tlb.UP_ERR_ALIGN
+    assert call_compact(src=(FAKE + 2,)) == tlb.UP_ERR_ALIGN
+    assert call_compact(wsb=tlb.compact_workspace_bytes(2, 1000) - 1) == tlb.UP_ERR_WORKSPACE
+
+
+def test_scatter_and_metadata_reject():
+    sb = lambda **kw: tlb.scatter_back(kw.get("c", FAKE), kw.get("rb", 16), kw.get("im", FAKE), FAKE,
+                                       kw.get("R", 1), 10, kw.get("full", FAKE), kw.get("fr", 10),
+                                       stream=0, raise_on_error=False)
+    assert sb(c=None) == tlb.UP_ERR_NULL
+    assert sb(full=None) == tlb.UP_ERR_NULL
+    assert sb(rb=3) == tlb.UP_ERR_PARAM
+    assert sb(R=-1) == tlb.UP_ERR_SHAPE
+    assert sb(fr=-1) == tlb.UP_ERR_SHAPE
+    assert sb(c=FAKE + 1) == tlb.UP_ERR_ALIGN
+    md = lambda **kw: tlb.update_metadata(kw.get("layer", 0), 4, kw.get("R", 1), FAKE, FAKE,
+                                          kw.get("sl", FAKE), FAKE, FAKE, kw.get("dl", FAKE), FAKE,
+                                          kw.get("md", 4), FAKE, stream=0, raise_on_error=False)
+    assert md(layer=-1) == tlb.UP_ERR_SHAPE
+    assert md(R=-1) == tlb.UP_ERR_SHAPE
+    assert md(sl=None) == tlb.UP_ERR_NULL
+    assert md(dl=None) == tlb.UP_ERR_NULL
+    assert md(md=-1) == tlb.UP_ERR_SHAPE
+
+
+def test_python_binding_raises():
+    with pytest.raises(tlb.UniPrefillError):
+        call = tlb.select_blocks(p(head_dim=96), FAKE, 1, FAKE, 1, FAKE, 1, 1, None, None, None, None,
+                                 FAKE, FAKE, FAKE, workspace_bytes=1, stream=0)
+        del call

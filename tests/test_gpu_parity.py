@@ -1,0 +1,333 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every input comes from the seeded generators in synth/ (or is drawn here from
+a seeded NumPy generator); every expected value comes from oracle/.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import token_level_block_amd as tlb  # noqa: E402
+from token_level_block_amd.runner import CompactBuffers, MetadataBuffers, SelectBuffers, run_scatter_back  # noqa: E402
+
+from gpu_helpers import check_masks, check_scores, dev, upload_qk  # noqa: E402
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_select(wl, cu, q, k, max_tokens=None):
+    T = int(cu[-1])
+    max_tokens = T if max_tokens is None else max_tokens
+    prm = tlb.make_params(wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p)
+    bufs = SelectBuffers.allocate(prm, wl.num_reqs, max_tokens)
+    bufs.keep_mask.fill_(0xAB)
+    cu_d, qd, kd = upload_qk(wl, cu, q, k)
+    bufs.run(qd, kd, cu_d)
+    torch.cuda.synchronize()
+    offs = bufs.block_offsets[: wl.num_reqs + 1].cpu().numpy()
+    nbt = int(offs[-1])
+    return dict(
+        offs=offs,
+        b=bufs.block_scores[:nbt].cpu().numpy(),
+        keep=bufs.keep_block[:nbt].cpu().numpy(),
+        mask=bufs.keep_mask[:T].cpu().numpy(),
+        kept=bufs.kept[: wl.num_reqs].cpu().numpy(),
+        bufs=bufs,
+    )
+
+
+def check_select(wl, label=""):
+    say(f"[select] {label} {wl.name} lengths={wl.lengths[:6]} hq={wl.hq} hkv={wl.hkv} d={wl.d} G={wl.G} "
+        f"A={wl.A} n={wl.n} p={wl.p}")
+    cu, q, k = synth.make_qk(wl)
+    ref = oracle.select(q, k, cu, wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p)
+    got = run_select(wl, cu, q, k)
+    assert np.array_equal(got["offs"], ref["block_offsets"])
+    check_scores(got["b"], ref["b64"], ref["block_offsets"])
+    mism = check_masks(ref, got["keep"], got["mask"], got["kept"], cu, wl)
+    return ref, got, mism
+
+
+TINY_CASES = [
+    # lengths, hq, hkv, d, G, A, n, p, kind
+    ((40,), 4, 2, 64, 32, 8, 8, 0.9, "hot"),
+    ((1, 5, 33, 64, 65, 100), 4, 1, 64, 32, 4, 8, 0.95, "hot"),
+    ((0, 300, 0, 129), 8, 2, 128, 32, 16, 16, 0.99, "powerlaw"),
+    ((2500,), 8, 2, 128, 64, 128, 128, 0.99, "powerlaw"),
+    ((1100, 3000, 77), 4, 4, 128, 64, 32, 100, 0.9, "hot"),
+    ((5000,), 16, 2, 256, 128, 128, 128, 0.99, "powerlaw"),
+    ((700, 1500), 16, 8, 256, 32, 64, 64, 0.98, "hot"),
+    ((96, 128, 200), 2, 2, 64, 96, 0, 1, 1.0, "powerlaw"),
+    ((4096,), 32, 8, 128, 64, 128, 128, 0.99, "hot"),
+    ((70,) * 16, 4, 2, 64, 32, 8, 8, 0.9, "powerlaw"),
+    ((3000,), 4, 2, 128, 64, 128, 256, 0.99, "powerlaw"),    # query slice split over grid z
+]
+
+
+@pytest.mark.parametrize("idx", range(len(TINY_CASES)), ids=[f"t{i}" for i in range(len(TINY_CASES))])
+def test_select_small_shapes(idx):
+    lengths, hq, hkv, d, G, A, n, p, kind = TINY_CASES[idx]
+    wl = synth.tiny(lengths, hq=hq, hkv=hkv, d=d, G=G, A=A, n=n, p=p, seed=100 + idx,
+                    kind=kind, hot=3, hot_lambda=6.0, c=1.5)
+    check_select(wl)
+
+
+def test_select_repeatable():
+    wl = synth.tiny((3000, 900), hq=8, hkv=2, d=128, G=64, A=128, n=128, p=0.99, seed=7, kind="powerlaw", c=1.4)
+    cu, q, k = synth.make_qk(wl)
+    a = run_select(wl, cu, q, k)
+    b = run_select(wl, cu, q, k)
+    for key in ("b", "keep", "mask", "kept"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.array_equal(a["b"].view(np.uint32), b["b"].view(np.uint32))
+
+
+def test_select_max_tokens_larger_than_stream():
+    wl = synth.tiny((500, 260), hq=4, hkv=2, d=64, G=32, A=8, n=16, p=0.95, seed=3)
+    cu, q, k = synth.make_qk(wl)
+    ref = oracle.select(q, k, cu, wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p)
+    got = run_select(wl, cu, q, k, max_tokens=int(cu[-1]) + 1000)
+    check_scores(got["b"], ref["b64"], ref["block_offsets"])
+    check_masks(ref, got["keep"], got["mask"], got["kept"], cu, wl)
+
+
+# ---------------------------------------------------------------------------
+# top-p from given scores: bit-exact
+# ---------------------------------------------------------------------------
+def _scores_case(seed, lengths, G, kinds):
+    rng = np.random.default_rng(seed)
+    nbs = [-(-L // G) for L in lengths]
+    parts = []
+    for r, nb in enumerate(nbs):
+        parts.append(synth.random_scores(rng, nb, kinds[r % len(kinds)]))
+    return np.concatenate(parts) if parts else np.zeros(0, np.float32)
+
+
+@pytest.mark.parametrize("seed,lengths,G,A,n,p,kinds", [
+    (0, (1000, 64, 1, 0, 4096), 64, 128, 128, 0.99, ("lognormal", "ties", "sparse", "pareto")),
+    (1, (777, 3333), 7, 5, 9, 0.9, ("ties", "lognormal")),
+    (2, (131072,), 64, 128, 128, 0.99, ("pareto",)),
+    (3, (65536,), 32, 128, 128, 0.98, ("lognormal",)),
+    (4, (5000, 6000, 7000), 128, 0, 1, 1.0, ("sparse", "ties", "lognormal")),
+    (5, tuple([300] * 16), 16, 16, 16, 0.5, ("ties", "lognormal", "pareto", "sparse")),
+])
+def test_topp_scores_in_bit_exact(seed, lengths, G, A, n, p, kinds):
+    say(f"[topp] seed={seed} lengths={lengths[:5]} G={G} p={p}")
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    sc = _scores_case(seed, lengths, G, kinds)
+    if seed == 0:   # values that carry no mass: zeros, -0, negatives, inf, nan
+        sc[3] = 0.0
+        sc[4] = -0.0
+        sc[5] = -2.5
+        sc[16] = np.inf
+        sc[17] = np.nan
+    R = len(lengths)
+    ref = oracle.select(None, None, cu, 1, 1, 1, G, A, n, p, scores_in=sc)
+    prm = tlb.make_params(1, 1, 1, G, A, n, p, scores_in=True)
+    bufs = SelectBuffers.allocate(prm, R, T)
+    bufs.block_scores.fill_(-1)
+    bufs.run(None, None, dev(cu), scores_in=dev(sc))
+    torch.cuda.synchronize()
+    nbt = len(sc)
+    assert np.array_equal(bufs.block_offsets[: R + 1].cpu().numpy(), ref["block_offsets"])
+    assert np.array_equal(bufs.keep_block[:nbt].cpu().numpy(), ref["keep_block"])
+    assert np.array_equal(bufs.keep_mask[:T].cpu().numpy(), ref["mask"])
+    assert np.array_equal(bufs.kept[:R].cpu().numpy(), ref["kept"])
+    assert np.array_equal(bufs.block_scores[:nbt].cpu().numpy().view(np.uint32), sc.view(np.uint32))
+
+
+def test_topp_fixture_through_gpu():
+    from pins import load_golden
+    g = load_golden("expand_hand_example.json")
+    sc = np.array(g["scores_times_64"], np.float32) / 64
+    cu = np.array([0, g["N"]], np.int32)
+    prm = tlb.make_params(1, 1, 1, g["G"], g["A"], g["n"], g["p"], scores_in=True)
+    bufs = SelectBuffers.allocate(prm, 1, g["N"])
+    bufs.run(None, None, dev(cu), scores_in=dev(sc))
+    torch.cuda.synchronize()
+    assert bufs.keep_mask[: g["N"]].cpu().tolist() == g["mask"]
+    assert int(bufs.kept[0]) == g["kept_tokens"]
+
+
+# ---------------------------------------------------------------------------
+# compaction, scatter-back, metadata: bit-exact
+# ---------------------------------------------------------------------------
+COMPACT_CASES = [
+    (0, (5000, 0, 3000, 9000), 0.4, (8192, 12, 4)),
+    (1, (1, 2, 3), 0.5, (16,)),
+    (2, (131072,), 0.4, (8192,)),
+    (3, tuple([4100] * 5), 0.9, (7680, 4096)),
+    (4, (300, 0), 0.0, (32,)),
+    (5, (70000,), 1.0, (4,)),
+]
+
+
+@pytest.mark.parametrize("seed,lengths,rho,row_bytes", COMPACT_CASES)
+def test_compact_and_scatter_bit_exact(seed, lengths, rho, row_bytes):
+    say(f"[compact] seed={seed} lengths={lengths[:5]} rho={rho} row_bytes={row_bytes}")
+    rng = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    R = len(lengths)
+    max_tokens = T + 37
+    mask = np.zeros(max_tokens, np.uint8)
+    mask[:T] = (rng.random(T) < rho).astype(np.uint8) * rng.integers(1, 256, T).astype(np.uint8)
+    mask[T:] = 1          # beyond the stream: must be ignored
+    bufs_h = [rng.integers(0, 2 ** 32, size=(max_tokens, rb // 4), dtype=np.uint64).astype(np.uint32)
+              for rb in row_bytes]
+    index_in = rng.permutation(10 * max_tokens)[:max_tokens].astype(np.int32)
+    for use_index in (False, True):
+        outs, idx, cu_out = oracle.compact(mask, cu, bufs_h, index_in if use_index else None)
+        src = [dev(b.view(np.int32)) for b in bufs_h]
+        dst = [torch.full_like(s, -7) for s in src]
+        cb = CompactBuffers.allocate(R, max_tokens)
+        cb.index_out.fill_(-5)
+        cb.run(dev(mask), dev(cu), src, dst, index_in=dev(index_in) if use_index else None)
+        torch.cuda.synchronize()
+        K = len(idx)
+        assert np.array_equal(cb.cu_out[: R + 1].cpu().numpy(), cu_out)
+        assert np.array_equal(cb.index_out[:K].cpu().numpy(), idx)
+        assert (cb.index_out[K:max_tokens].cpu().numpy() == -5).all()
+        for o, d in zip(outs, dst):
+            got = d[:K].cpu().numpy().view(np.uint32)
+            assert np.array_equal(got, o)
+            assert (d[K:].cpu().numpy() == -7).all()
+        if not use_index:
+            # Eq. 8: scatter processed rows (x + 1) back into the full buffers
+            for b, (o, d) in enumerate(zip(outs, dst)):
+                proc = (o.astype(np.uint64) + 1).astype(np.uint32)
+                want = oracle.scatter_back(bufs_h[b], proc, idx, K)
+                full = dev(bufs_h[b].view(np.int32))
+                run_scatter_back(dev(proc.view(np.int32)) if K else torch.zeros((1, proc.shape[1]), dtype=torch.int32, device="cuda"),
+                                 cb.index_out, cb.cu_out, R, max_tokens, full)
+                torch.cuda.synchronize()
+                assert np.array_equal(full.cpu().numpy().view(np.uint32), want)
+
+
+def test_compact_twice_composes_index():
+    rng = np.random.default_rng(11)
+    lengths = (6000, 2500, 9000)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    H = rng.integers(0, 2 ** 32, size=(T, 8), dtype=np.uint64).astype(np.uint32)
+    m1 = (rng.random(T) < 0.6).astype(np.uint8)
+    (h1,), i1, cu1 = oracle.compact(m1, cu, [H])
+    m2 = (rng.random(len(i1)) < 0.5).astype(np.uint8)
+    (h2,), i2, cu2 = oracle.compact(m2, cu1, [h1], index_in=i1)
+    Hd = dev(H.view(np.int32))
+    d1 = torch.empty_like(Hd)
+    c1 = CompactBuffers.allocate(3, T)
+    c1.run(dev(m1), dev(cu), [Hd], [d1])
+    d2 = torch.empty_like(Hd)
+    c2 = CompactBuffers.allocate(3, T)
+    m2d = torch.zeros(T, dtype=torch.uint8, device="cuda")
+    m2d[: len(m2)] = dev(m2)
+    c2.run(m2d, c1.cu_out, [d1], [d2], index_in=c1.index_out)
+    torch.cuda.synchronize()
+    K = len(i2)
+    assert np.array_equal(c2.index_out[:K].cpu().numpy(), i2)
+    assert np.array_equal(c2.cu_out.cpu().numpy(), cu2)
+    assert np.array_equal(d2[:K].cpu().numpy().view(np.uint32), h2)
+
+
+def test_metadata_and_eq17():
+    rng = np.random.default_rng(5)
+    R, L, max_drops = 6, 32, 3
+    lens = rng.integers(50, 400, R)
+    ctx = rng.integers(0, 30, R)
+    orig = lens + ctx
+    st = oracle.MetadataState.fresh(orig)
+    mb = MetadataBuffers.allocate(orig, L, max_drops)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    layers = [3, 9, 17, 25]      # one more drop than the history can hold
+    for layer in layers:
+        cur = np.diff(cu)
+        kept = np.array([int(rng.integers(0, c + 1)) for c in cur])
+        cu_new = np.concatenate([[0], np.cumsum(kept)]).astype(np.int32)
+        st, nat = oracle.update_metadata(st, layer, cu, cu_new)
+        mb.run(layer, dev(cu), dev(cu_new))
+        torch.cuda.synchronize()
+        assert int(mb.num_actual_tokens[0]) == nat
+        assert np.array_equal(mb.seq_lens.cpu().numpy(), st.seq_lens)
+        cu = cu_new
+    assert np.array_equal(mb.drop_count.cpu().numpy(), np.full(R, len(layers)))
+    dl = mb.drop_layer.cpu().numpy().reshape(R, max_drops)
+    dn = mb.drop_len.cpu().numpy().reshape(R, max_drops)
+    for r in range(R):
+        assert [(int(a), int(b)) for a, b in zip(dl[r], dn[r])] == st.history[r][:max_drops]
+    base = mb.seqused_base.cpu().numpy().reshape(L, R)
+    kv_len = orig + rng.integers(0, 20, R)
+    for lp in range(L):
+        for r in range(R):
+            want = oracle.seqused_eq17(st.history[r], lp, int(orig[r]), int(kv_len[r]))
+            assert int(base[lp, r]) + int(kv_len[r] - orig[r]) == want, (lp, r)
+
+
+# ---------------------------------------------------------------------------
+# the workloads at full size
+# ---------------------------------------------------------------------------
+def test_llama_4k_single_request():
+    ref, got, mism = check_select(synth.llama_4k())
+    say(f"  kept={got['kept'].tolist()} mismatched blocks={mism}")
+
+
+def test_llama_varlen_batch():
+    ref, got, mism = check_select(synth.llama_varlen4())
+    say(f"  kept={got['kept'].tolist()} of {list(synth.llama_varlen4().lengths)} mismatched={mism}")
+
+
+@pytest.mark.parametrize("model", ["qwen_next", "gemma3"])
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_hybrid_64k(model, G):
+    wl = synth.hybrid_64k(model, G, p=0.98 if model == "gemma3" else 0.99)
+    ref, got, mism = check_select(wl)
+    say(f"  kept={got['kept'].tolist()} mismatched={mism}")
+
+
+def test_llama_128k_end_to_end():
+    """Select, compact hidden rows, patch metadata, scatter back: the bench's
+    workload at full size, checked against the oracle."""
+    wl = synth.llama_128k()
+    ref, got, mism = check_select(wl)
+    cu = wl.cu_seqlens()
+    T = int(cu[-1])
+    mask_ref = ref["mask"]
+    _, idx_ref, cu_out_ref = oracle.compact(mask_ref, cu, [])
+    nwords = wl.hidden // 2
+    hidden = synth.hidden_words_torch(0, T, nwords, "cuda")
+    out = torch.empty_like(hidden)
+    cb = CompactBuffers.allocate(1, T)
+    cb.run(dev(mask_ref), dev(cu), [hidden], [out])
+    torch.cuda.synchronize()
+    K = len(idx_ref)
+    assert np.array_equal(cb.index_out[:K].cpu().numpy(), idx_ref)
+    assert np.array_equal(cb.cu_out.cpu().numpy(), cu_out_ref)
+    # compacted rows equal the index-encoded rows of the oracle's kept tokens
+    for a in range(0, K, 8192):
+        z = min(K, a + 8192)
+        want = torch.from_numpy(synth.hidden_words(idx_ref[a:z], nwords).view(np.int32)).cuda()
+        assert torch.equal(out[a:z], want)
+    # Eq. 8 with processed = compacted + 1 on kept rows
+    full = hidden.clone()
+    run_scatter_back(out[:K] + 1, cb.index_out, cb.cu_out, 1, T, full)
+    torch.cuda.synchronize()
+    keep = torch.from_numpy(mask_ref.astype(bool)).cuda()
+    assert torch.equal(full[~keep], hidden[~keep])
+    assert torch.equal(full[keep], hidden[keep] + 1)
+    say(f"  kept tokens={int(got['kept'][0])} ({got['kept'][0] / T:.3f}) blocks kept="
+        f"{int(got['keep'].sum())}/{len(got['keep'])} mismatched={mism}")

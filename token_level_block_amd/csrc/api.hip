@@ -1,0 +1,290 @@
+// C ABI of libuniprefill: argument validation, workspace layout and launch
+// order.  Every check runs on the host before anything is enqueued, so a bad
+// argument leaves all buffers untouched.
+#include <math.h>
+
+#include "../../include/uniprefill.h"
+#include "common.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int32_t chunk_keys_for(int32_t G) {
+  // keys per score workgroup: a multiple of G near 1024
+  const int32_t m = G >= 1024 ? 1 : 1024 / G;
+  return G * m;
+}
+
+struct SelectLayout {
+  size_t cu, blk, chunk, keep, scores, chunk_lse, lse, row_lse, total;
+  int64_t max_blocks, max_chunks;
+  int32_t chunk_keys;
+  bool scoring;
+};
+
+up_status check_select_params(const up_select_params* prm) {
+  if (prm == nullptr) return UP_ERR_NULL;
+  const bool scoring = (prm->flags & UP_SCORES_IN) == 0u;
+  if (prm->flags & ~UP_SCORES_IN) return UP_ERR_PARAM;
+  if (prm->num_heads_q < 1 || prm->num_heads_kv < 1) return UP_ERR_SHAPE;
+  if (prm->num_heads_q % prm->num_heads_kv != 0) return UP_ERR_SHAPE;
+  if (prm->block_size < 1 || prm->num_sink < 0 || prm->window < 1) return UP_ERR_PARAM;
+  if (!(prm->top_p > 0.0 && prm->top_p <= 1.0)) return UP_ERR_PARAM;   // also rejects NaN
+  if (scoring) {
+    if (prm->head_dim != 64 && prm->head_dim != 128 && prm->head_dim != 256) return UP_ERR_PARAM;
+    if (prm->block_size % 32 != 0) return UP_ERR_PARAM;
+    if (!(isfinite(prm->softmax_scale))) return UP_ERR_PARAM;
+    // rows of the block-partial workspace are indexed with 32-bit offsets per block
+    if ((int64_t)prm->num_heads_q * prm->window > (1 << 24)) return UP_ERR_PARAM;
+  } else {
+    if (prm->head_dim < 1) return UP_ERR_PARAM;
+  }
+  return UP_OK;
+}
+
+up_status plan_select(const up_select_params* prm, int32_t R, int64_t max_tokens, SelectLayout* L) {
+  up_status st = check_select_params(prm);
+  if (st != UP_OK) return st;
+  if (R < 0 || max_tokens < 0 || max_tokens > INT32_MAX) return UP_ERR_SHAPE;
+  const int32_t G = prm->block_size;
+  L->scoring = (prm->flags & UP_SCORES_IN) == 0u;
+  L->chunk_keys = chunk_keys_for(G);
+  L->max_blocks = max_tokens / G + R;
+  L->max_chunks = max_tokens / L->chunk_keys + R;
+  const int64_t rows = (int64_t)prm->num_heads_q * prm->window;
+  size_t off = 0;
+  L->cu = off;      off = align_up(off + sizeof(int32_t) * (size_t)(R + 1));
+  L->blk = off;     off = align_up(off + sizeof(int32_t) * (size_t)(R + 1));
+  L->chunk = off;   off = align_up(off + sizeof(int32_t) * (size_t)(R + 1));
+  L->keep = off;    off = align_up(off + (size_t)L->max_blocks);
+  L->scores = off;  off = align_up(off + sizeof(float) * (size_t)L->max_blocks);
+  if (L->scoring) {
+    L->chunk_lse = off; off = align_up(off + sizeof(float) * (size_t)L->max_chunks * (size_t)rows);
+    L->lse = off;       off = align_up(off + sizeof(float) * (size_t)L->max_blocks * (size_t)rows);
+    L->row_lse = off;   off = align_up(off + sizeof(float) * (size_t)R * (size_t)rows);
+  } else {
+    L->chunk_lse = L->lse = L->row_lse = off;
+  }
+  L->total = off;
+  return UP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* up_status_string(up_status s) {
+  switch (s) {
+    case UP_OK: return "ok";
+    case UP_ERR_NULL: return "a required pointer is NULL";
+    case UP_ERR_SHAPE: return "inconsistent sizes";
+    case UP_ERR_PARAM: return "parameter out of the supported range";
+    case UP_ERR_WORKSPACE: return "workspace too small";
+    case UP_ERR_ALIGN: return "pointer or stride not aligned as required";
+    case UP_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int64_t up_max_blocks(int32_t block_size, int32_t num_reqs, int64_t max_tokens) {
+  if (block_size < 1 || num_reqs < 0 || max_tokens < 0) return -1;
+  return max_tokens / block_size + num_reqs;
+}
+
+size_t up_select_workspace_bytes(const up_select_params* prm, int32_t num_reqs, int64_t max_tokens) {
+  SelectLayout L;
+  if (plan_select(prm, num_reqs, max_tokens, &L) != UP_OK) return 0;
+  return L.total;
+}
+
+up_status up_select_blocks(const up_select_params* prm, const void* q, int64_t q_row_stride,
+                           const void* k, int64_t k_row_stride, const int32_t* cu_seqlens,
+                           int32_t num_reqs, int64_t max_tokens, const float* scores_in,
+                           float* block_scores, int32_t* block_offsets, uint8_t* keep_block,
+                           uint8_t* keep_mask, int32_t* kept_per_req, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  SelectLayout L;
+  up_status st = plan_select(prm, num_reqs, max_tokens, &L);
+  if (st != UP_OK) return st;
+  if (cu_seqlens == nullptr || keep_mask == nullptr || kept_per_req == nullptr || workspace == nullptr)
+    return UP_ERR_NULL;
+  if (L.scoring) {
+    if (q == nullptr || k == nullptr) return UP_ERR_NULL;
+    const int64_t d = prm->head_dim;
+    if (q_row_stride < prm->num_heads_q * d || k_row_stride < prm->num_heads_kv * d) return UP_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(k, 16) || q_row_stride % 8 != 0 || k_row_stride % 8 != 0)
+      return UP_ERR_ALIGN;
+  } else {
+    if (scores_in == nullptr) return UP_ERR_NULL;
+  }
+  if (!aligned(workspace, kAlign)) return UP_ERR_ALIGN;
+  if (workspace_bytes < L.total) return UP_ERR_WORKSPACE;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  up::Offsets off;
+  off.cu = reinterpret_cast<int32_t*>(ws + L.cu);
+  off.blk = reinterpret_cast<int32_t*>(ws + L.blk);
+  off.chunk = reinterpret_cast<int32_t*>(ws + L.chunk);
+  uint8_t* keep = keep_block ? keep_block : (ws + L.keep);
+  const int32_t R = num_reqs;
+
+  if (up::launch_prep(cu_seqlens, R, max_tokens, prm->block_size, L.chunk_keys, off, block_offsets,
+                      stream) != hipSuccess)
+    return UP_ERR_HIP;
+
+  const float* scores = scores_in;
+  float* scores_copy = nullptr;
+  if (L.scoring) {
+    float* out = block_scores ? block_scores : reinterpret_cast<float*>(ws + L.scores);
+    const double scale = prm->softmax_scale > 0.f ? (double)prm->softmax_scale
+                                                  : 1.0 / sqrt((double)prm->head_dim);
+    up::ScoreArgs sa;
+    sa.q = static_cast<const uint16_t*>(q);
+    sa.k = static_cast<const uint16_t*>(k);
+    sa.q_stride = q_row_stride;
+    sa.k_stride = k_row_stride;
+    sa.off = off;
+    sa.R = R;
+    sa.hq = prm->num_heads_q;
+    sa.hkv = prm->num_heads_kv;
+    sa.d = prm->head_dim;
+    sa.G = prm->block_size;
+    sa.n = prm->window;
+    sa.chunk_keys = L.chunk_keys;
+    sa.c = (float)(scale * 1.4426950408889634074);
+    sa.lse = reinterpret_cast<float*>(ws + L.lse);
+    sa.chunk_lse = reinterpret_cast<float*>(ws + L.chunk_lse);
+    sa.max_chunks = L.max_chunks;
+    if (prm->prof_score_begin && hipEventRecord((hipEvent_t)prm->prof_score_begin, stream) != hipSuccess)
+      return UP_ERR_HIP;
+    if (up::launch_score(sa, stream) != hipSuccess) return UP_ERR_HIP;
+    if (prm->prof_score_end && hipEventRecord((hipEvent_t)prm->prof_score_end, stream) != hipSuccess)
+      return UP_ERR_HIP;
+    up::CombineArgs ca;
+    ca.off = off;
+    ca.R = R;
+    ca.hq = prm->num_heads_q;
+    ca.n = prm->window;
+    ca.G = prm->block_size;
+    ca.lse = sa.lse;
+    ca.chunk_lse = sa.chunk_lse;
+    ca.row_lse = reinterpret_cast<float*>(ws + L.row_lse);
+    ca.scores = out;
+    ca.max_blocks = L.max_blocks;
+    if (up::launch_combine(ca, stream) != hipSuccess) return UP_ERR_HIP;
+    scores = out;
+  } else {
+    scores_copy = block_scores;
+  }
+
+  up::ToppArgs ta;
+  ta.off = off;
+  ta.R = R;
+  ta.G = prm->block_size;
+  ta.A = prm->num_sink;
+  ta.n = prm->window;
+  ta.p = prm->top_p;
+  ta.scores = scores;
+  ta.scores_copy = scores_copy;
+  ta.keep_block = keep;
+  ta.mask = keep_mask;
+  ta.kept = kept_per_req;
+  ta.max_tokens = max_tokens;
+  ta.max_blocks = L.max_blocks;
+  if (up::launch_topp(ta, stream) != hipSuccess) return UP_ERR_HIP;
+  return UP_OK;
+}
+
+size_t up_compact_workspace_bytes(int32_t num_reqs, int64_t max_tokens) {
+  if (num_reqs < 0 || max_tokens < 0 || max_tokens > INT32_MAX) return 0;
+  const int64_t ntiles = (max_tokens + up::kCountTile - 1) / up::kCountTile;
+  size_t off = align_up(sizeof(int32_t) * (size_t)(num_reqs + 1));
+  off = align_up(off + sizeof(int32_t) * (size_t)ntiles);
+  off = align_up(off + sizeof(int32_t) * (size_t)(ntiles + 1));
+  return off;
+}
+
+up_status up_compact(const uint8_t* keep_mask, const int32_t* cu_seqlens, int32_t num_reqs,
+                     int64_t max_tokens, int32_t num_buffers, const void* const* src,
+                     void* const* dst, const int64_t* row_bytes, const int32_t* index_in,
+                     int32_t* index_out, int32_t* cu_seqlens_out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  if (num_reqs < 0 || max_tokens < 0 || max_tokens > INT32_MAX) return UP_ERR_SHAPE;
+  if (num_buffers < 0 || num_buffers > up::kMaxCompactBuffers) return UP_ERR_PARAM;
+  if (keep_mask == nullptr || cu_seqlens == nullptr || index_out == nullptr ||
+      cu_seqlens_out == nullptr || workspace == nullptr)
+    return UP_ERR_NULL;
+  if (num_buffers > 0 && (src == nullptr || dst == nullptr || row_bytes == nullptr)) return UP_ERR_NULL;
+  up::CompactArgs a;
+  a.bufs.nbuf = num_buffers;
+  for (int b = 0; b < num_buffers; ++b) {
+    if (src[b] == nullptr || dst[b] == nullptr) return UP_ERR_NULL;
+    if (row_bytes[b] <= 0 || row_bytes[b] % 4 != 0) return UP_ERR_PARAM;
+    if (!aligned(src[b], 4) || !aligned(dst[b], 4)) return UP_ERR_ALIGN;
+    a.bufs.src[b] = static_cast<const uint8_t*>(src[b]);
+    a.bufs.dst[b] = static_cast<uint8_t*>(dst[b]);
+    a.bufs.row_bytes[b] = row_bytes[b];
+    a.bufs.vec16[b] = (row_bytes[b] % 16 == 0 && aligned(src[b], 16) && aligned(dst[b], 16)) ? 1 : 0;
+  }
+  if (!aligned(keep_mask, 16) || !aligned(workspace, kAlign)) return UP_ERR_ALIGN;
+  const size_t need = up_compact_workspace_bytes(num_reqs, max_tokens);
+  if (workspace_bytes < need) return UP_ERR_WORKSPACE;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int64_t ntiles = (max_tokens + up::kCountTile - 1) / up::kCountTile;
+  size_t off = 0;
+  a.cu_s = reinterpret_cast<int32_t*>(ws + off);
+  off = align_up(off + sizeof(int32_t) * (size_t)(num_reqs + 1));
+  a.tile_count = reinterpret_cast<int32_t*>(ws + off);
+  off = align_up(off + sizeof(int32_t) * (size_t)ntiles);
+  a.tile_prefix = reinterpret_cast<int32_t*>(ws + off);
+  a.num_count_tiles = ntiles;
+  a.mask = keep_mask;
+  a.cu_in = cu_seqlens;
+  a.R = num_reqs;
+  a.max_tokens = max_tokens;
+  a.index_in = index_in;
+  a.index_out = index_out;
+  a.cu_out = cu_seqlens_out;
+  if (up::launch_compact(a, stream) != hipSuccess) return UP_ERR_HIP;
+  return UP_OK;
+}
+
+up_status up_scatter_back(const void* compacted, int64_t row_bytes, const int32_t* index_map,
+                          const int32_t* cu_seqlens_out, int32_t num_reqs, int64_t max_tokens,
+                          void* full, int64_t full_rows, hipStream_t stream) {
+  if (num_reqs < 0 || max_tokens < 0 || max_tokens > INT32_MAX || full_rows < 0) return UP_ERR_SHAPE;
+  if (compacted == nullptr || index_map == nullptr || cu_seqlens_out == nullptr || full == nullptr)
+    return UP_ERR_NULL;
+  if (row_bytes <= 0 || row_bytes % 4 != 0) return UP_ERR_PARAM;
+  if (!aligned(compacted, 4) || !aligned(full, 4)) return UP_ERR_ALIGN;
+  if (up::launch_scatter(compacted, row_bytes, index_map, cu_seqlens_out + num_reqs, max_tokens, full,
+                         full_rows, stream) != hipSuccess)
+    return UP_ERR_HIP;
+  return UP_OK;
+}
+
+up_status up_update_metadata(int32_t layer, int32_t num_layers, int32_t num_reqs,
+                             const int32_t* cu_seqlens_old, const int32_t* cu_seqlens_new,
+                             int32_t* seq_lens, int32_t* num_actual_tokens, int32_t* drop_count,
+                             int32_t* drop_layer, int32_t* drop_len, int32_t max_drops,
+                             int32_t* seqused_base, hipStream_t stream) {
+  if (num_reqs < 0 || layer < 0 || max_drops < 0) return UP_ERR_SHAPE;
+  if (seqused_base != nullptr && num_layers < 0) return UP_ERR_SHAPE;
+  if (cu_seqlens_old == nullptr || cu_seqlens_new == nullptr || seq_lens == nullptr ||
+      num_actual_tokens == nullptr || drop_count == nullptr)
+    return UP_ERR_NULL;
+  if (max_drops > 0 && (drop_layer == nullptr || drop_len == nullptr)) return UP_ERR_NULL;
+  if (up::launch_metadata(layer, seqused_base ? num_layers : 0, num_reqs, cu_seqlens_old,
+                          cu_seqlens_new, seq_lens, num_actual_tokens, drop_count, drop_layer,
+                          drop_len, max_drops, seqused_base, stream) != hipSuccess)
+    return UP_ERR_HIP;
+  return UP_OK;
+}
+
+}  // extern "C"

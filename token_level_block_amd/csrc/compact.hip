@@ -1,0 +1,253 @@
+// Compaction of the packed token stream and the carry-forward scatter
+// (UniPrefill Sec. 3.4 Eq. 7-8; Sec. 3.5, the compacted stream that the
+// patched query_start_loc describes).
+//
+//   count  : one workgroup per 4096-token tile counts the set mask bytes;
+//   scan   : one workgroup clamps cu_seqlens and turns the tile counts into
+//            exclusive prefixes;
+//   gather : one workgroup per 256-token tile ranks its kept tokens (wave
+//            ballots), writes the index map and the new request offsets that
+//            fall in its tile, and copies the kept rows of every buffer with
+//            coalesced 16-byte accesses;
+//   scatter: every compacted row goes back to its original position.
+// No atomics and no inter-workgroup waiting: every result is deterministic.
+#include "common.h"
+
+namespace up {
+
+constexpr int kCountThreads = kCountTile / 16;   // 16 mask bytes per thread
+constexpr int kGatherThreads = kGatherTile;      // one token per thread
+constexpr int kScanThreads = 1024;
+constexpr int kScatterThreads = 256;
+constexpr int kScatterRows = 16;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// number of nonzero bytes in a 32-bit word
+__device__ __forceinline__ int nonzero_bytes(uint32_t w) {
+  const uint32_t hi = ((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w;   // 0x80 set in each nonzero byte
+  return __popc(hi & 0x80808080u);
+}
+
+__device__ __forceinline__ int count_piece(const uint8_t* mask, int64_t pos, int64_t limit) {
+  // nonzero bytes among mask[pos .. min(pos+16, limit))
+  if (pos + 16 <= limit) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(mask + pos);
+    return nonzero_bytes(v[0]) + nonzero_bytes(v[1]) + nonzero_bytes(v[2]) + nonzero_bytes(v[3]);
+  }
+  int c = 0;
+  for (int64_t i = pos; i < limit; ++i) c += mask[i] != 0;
+  return c;
+}
+
+// One wave copies one row: 16-byte pieces, eight loads in flight per lane.
+__device__ __forceinline__ void copy_row_vec(const uint8_t* __restrict__ sp, uint8_t* __restrict__ dp,
+                                             int cpr, int lane) {
+  int part = lane;
+  for (; part + 7 * kWave < cpr; part += 8 * kWave) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const u32x4*>(sp + (int64_t)(part + u * kWave) * 16);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) *reinterpret_cast<u32x4*>(dp + (int64_t)(part + u * kWave) * 16) = v[u];
+  }
+  for (; part < cpr; part += kWave)
+    *reinterpret_cast<u32x4*>(dp + (int64_t)part * 16) = *reinterpret_cast<const u32x4*>(sp + (int64_t)part * 16);
+}
+
+__device__ __forceinline__ void copy_row_words(const uint8_t* __restrict__ sp, uint8_t* __restrict__ dp,
+                                               int wpr, int lane) {
+  for (int part = lane; part < wpr; part += kWave)
+    *reinterpret_cast<uint32_t*>(dp + (int64_t)part * 4) = *reinterpret_cast<const uint32_t*>(sp + (int64_t)part * 4);
+}
+
+__global__ __launch_bounds__(kCountThreads) void count_kernel(const uint8_t* __restrict__ mask,
+                                                              int64_t max_tokens,
+                                                              int32_t* __restrict__ tile_count) {
+  __shared__ int32_t red[kCountThreads / kWave];
+  const int64_t pos = (int64_t)blockIdx.x * kCountTile + threadIdx.x * 16;
+  int c = pos < max_tokens ? count_piece(mask, pos, max_tokens) : 0;
+  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0;
+    for (int w = 0; w < kCountThreads / kWave; ++w) t += red[w];
+    tile_count[blockIdx.x] = t;
+  }
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ cu_in, int R,
+                                                            int64_t max_tokens,
+                                                            const int32_t* __restrict__ tile_count,
+                                                            int64_t ntiles, int32_t* __restrict__ cu_s,
+                                                            int32_t* __restrict__ tile_prefix,
+                                                            int32_t* __restrict__ cu_out) {
+  __shared__ int32_t scratch[kScanThreads / kWave];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x;
+  const int32_t cap = (int32_t)(max_tokens < 0x7fffffff ? max_tokens : 0x7fffffff);
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base <= R; base += kScanThreads) {
+    const int e = base + tid;
+    const int32_t v = (e <= R) ? max(0, min(cu_in[e], cap)) : 0;
+    const int32_t m = max(block_inclusive_scan<true>(v, scratch), carry);
+    if (e <= R) cu_s[e] = m;
+    __syncthreads();
+    if (tid == kScanThreads - 1) carry = m;
+    __syncthreads();
+  }
+  const int32_t T = carry;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < ntiles; base += kScanThreads) {
+    const int64_t t = base + tid;
+    const int32_t v = (t < ntiles) ? tile_count[t] : 0;
+    const int32_t incl = block_inclusive_scan<false>(v, scratch) + carry;
+    if (t < ntiles) tile_prefix[t] = incl - v;
+    if (t == ntiles - 1) tile_prefix[ntiles] = incl;
+    __syncthreads();
+    if (tid == kScanThreads - 1) carry = incl;
+    __syncthreads();
+  }
+  // an empty stream has no gather tile to report the request offsets
+  if (T == 0)
+    for (int e = tid; e <= R; e += kScanThreads) cu_out[e] = 0;
+}
+
+__global__ __launch_bounds__(kGatherThreads) void gather_kernel(CompactArgs a) {
+  __shared__ int32_t red[kGatherThreads / kWave];
+  __shared__ int32_t wsum[kGatherThreads / kWave];
+  __shared__ int32_t excl[kGatherThreads + 1];
+  __shared__ int32_t list[kGatherThreads];
+  __shared__ int32_t s_prefix;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t start = (int64_t)blockIdx.x * kGatherTile;
+  const int32_t T = a.cu_s[a.R];
+  if (start >= T) return;
+  const int64_t end = min<int64_t>(start + kGatherTile, T);
+
+  // kept tokens before this tile: the count tile's prefix plus the pieces of
+  // the count tile that precede this gather tile
+  const int64_t ct = start / kCountTile;
+  const int64_t cstart = ct * kCountTile;
+  int c = 0;
+  {
+    const int64_t pos = cstart + (int64_t)tid * 16;
+    if (pos < start) c = count_piece(a.mask, pos, start);
+  }
+  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+  if (lane == 0) red[wid] = c;
+  __syncthreads();
+  if (tid == 0) {
+    int t = a.tile_prefix[ct];
+    for (int w = 0; w < kGatherThreads / kWave; ++w) t += red[w];
+    s_prefix = t;
+  }
+
+  // rank the kept tokens of this tile
+  const int64_t i = start + tid;
+  const bool kept = (i < end) && a.mask[i] != 0;
+  const unsigned long long bal = __ballot(kept);
+  const int below = __popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) wsum[wid] = __popcll(bal);
+  __syncthreads();
+  int wpre = 0;
+  for (int w = 0; w < wid; ++w) wpre += wsum[w];
+  const int local = wpre + below;
+  excl[tid] = local;
+  if (tid == kGatherThreads - 1) excl[kGatherThreads] = local + (kept ? 1 : 0);
+  if (kept) list[local] = tid;
+  __syncthreads();
+  const int32_t prefix = s_prefix;
+  const int cnt = excl[kGatherThreads];
+
+  if (kept) a.index_out[prefix + local] = a.index_in ? a.index_in[i] : (int32_t)i;
+
+  // new request offsets that fall inside this tile (the last tile also owns position T)
+  for (int r = tid; r <= a.R; r += kGatherThreads) {
+    const int32_t p = a.cu_s[r];
+    if (p >= start && (p < end || (p == T && end == T)))
+      a.cu_out[r] = prefix + excl[p - start];
+  }
+
+  // copy kept rows of every buffer, one wave per row
+  constexpr int nw = kGatherThreads / kWave;
+  for (int b = 0; b < a.bufs.nbuf; ++b) {
+    const uint8_t* src = a.bufs.src[b];
+    uint8_t* dst = a.bufs.dst[b];
+    const int64_t rb = a.bufs.row_bytes[b];
+    const bool vec = a.bufs.vec16[b] != 0;
+    for (int row = wid; row < cnt; row += nw) {
+      const uint8_t* sp = src + (start + list[row]) * rb;
+      uint8_t* dp = dst + (int64_t)(prefix + row) * rb;
+      if (vec) copy_row_vec(sp, dp, (int)(rb >> 4), lane);
+      else copy_row_words(sp, dp, (int)(rb >> 2), lane);
+    }
+  }
+}
+
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
+  if (a.num_count_tiles > 0) {
+    hipLaunchKernelGGL(count_kernel, dim3((unsigned)a.num_count_tiles), dim3(kCountThreads), 0, s,
+                       a.mask, a.max_tokens, a.tile_count);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a.cu_in, (int)a.R, a.max_tokens,
+                     a.tile_count, a.num_count_tiles, a.cu_s, a.tile_prefix, a.cu_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ntiles = (a.max_tokens + kGatherTile - 1) / kGatherTile;
+  if (ntiles > 0) {
+    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)ntiles), dim3(kGatherThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Eq. 8 carry-forward: full[index_map[k]] = compacted[k], k < count
+// ---------------------------------------------------------------------------
+template <bool kVec>
+__global__ __launch_bounds__(kScatterThreads) void scatter_kernel(const uint8_t* __restrict__ src,
+                                                                  int64_t rb,
+                                                                  const int32_t* __restrict__ index_map,
+                                                                  const int32_t* __restrict__ count_ptr,
+                                                                  uint8_t* __restrict__ full,
+                                                                  int64_t full_rows, int64_t max_rows) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t k0 = (int64_t)blockIdx.x * kScatterRows;
+  const int64_t count = min<int64_t>(*count_ptr, max_rows);
+  if (k0 >= count) return;
+  const int nrows = (int)min<int64_t>(kScatterRows, count - k0);
+  constexpr int nw = kScatterThreads / kWave;
+  for (int row = wid; row < nrows; row += nw) {
+    const int32_t d = index_map[k0 + row];
+    if (d < 0 || d >= full_rows) continue;
+    const uint8_t* sp = src + (k0 + row) * rb;
+    uint8_t* dp = full + (int64_t)d * rb;
+    if (kVec) copy_row_vec(sp, dp, (int)(rb >> 4), lane);
+    else copy_row_words(sp, dp, (int)(rb >> 2), lane);
+  }
+}
+
+hipError_t launch_scatter(const void* compacted, int64_t row_bytes, const int32_t* index_map,
+                          const int32_t* count_ptr, int64_t max_tokens, void* full,
+                          int64_t full_rows, hipStream_t s) {
+  const int64_t nblk = (max_tokens + kScatterRows - 1) / kScatterRows;
+  if (nblk <= 0) return hipSuccess;
+  const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)compacted % 16 == 0) && ((uintptr_t)full % 16 == 0);
+  if (vec)
+    hipLaunchKernelGGL(scatter_kernel<true>, dim3((unsigned)nblk), dim3(kScatterThreads), 0, s,
+                       (const uint8_t*)compacted, row_bytes, index_map, count_ptr, (uint8_t*)full, full_rows,
+                       max_tokens);
+  else
+    hipLaunchKernelGGL(scatter_kernel<false>, dim3((unsigned)nblk), dim3(kScatterThreads), 0, s,
+                       (const uint8_t*)compacted, row_bytes, index_map, count_ptr, (uint8_t*)full, full_rows,
+                       max_tokens);
+  return hipGetLastError();
+}
+
+}  // namespace up

@@ -1,0 +1,209 @@
+// Top-p block selection and block-to-token expansion (UniPrefill Sec. 3.3
+// Eq. 5 and Sec. 3.5 Eq. 14 with the expansion step that follows it).
+//
+// Blocks are ranked by the packed key  (phi(b_g) << 32) | g  in descending
+// order, phi being the sign-bit-decided monotone map of Eq. 14.  Instead of
+// sorting, the kernel finds the pivot block pi(k*) directly: a weighted
+// most-significant-digit radix select over the 64-bit keys, whose weights
+// are the exact integer masses q_g = floor(b_g * 2^shift) (shift chosen so
+// that the total fits 52 bits).  The pivot is the largest key whose suffix
+// mass (over keys >= it) reaches thr = p * total; the kept blocks are exactly
+// the keys >= pivot.  Integer sums make the result independent of the order
+// of any reduction, so it matches a sequential sort-and-scan bit for bit.
+#include "common.h"
+
+namespace up {
+
+constexpr int kToppThreads = 512;
+constexpr int kToppWaves = kToppThreads / kWave;
+
+__device__ __forceinline__ uint32_t phi_bits(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b >> 31) ? ~b : (b ^ 0x80000000u);
+}
+
+// Positive and finite (excludes +0, negatives, inf, nan).
+__device__ __forceinline__ bool usable(uint32_t b) { return b != 0u && b < 0x7F800000u; }
+
+template <typename T>
+__device__ __forceinline__ T block_reduce(T v, T* red, bool is_max) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  for (int o = 32; o >= 1; o >>= 1) {
+    T x = __shfl_xor(v, o);
+    v = is_max ? (x > v ? x : v) : v + x;
+  }
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  T t = red[0];
+  for (int w = 1; w < kToppWaves; ++w) t = is_max ? (red[w] > t ? red[w] : t) : t + red[w];
+  __syncthreads();
+  return t;
+}
+
+__global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
+  __shared__ unsigned long long h_mass[256];
+  __shared__ uint32_t h_cnt[256];
+  __shared__ unsigned long long red64[kToppWaves];
+  __shared__ uint32_t red32[kToppWaves];
+  __shared__ unsigned long long s_above, s_key;
+  __shared__ int s_dsel;
+  __shared__ uint32_t s_cnt;
+
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int N = a.off.cu[r + 1] - a.off.cu[r];
+  const int b0 = a.off.blk[r];
+  const int nb = a.off.blk[r + 1] - b0;
+  if (nb <= 0) {
+    if (tid == 0) a.kept[r] = 0;
+    return;
+  }
+  const float* sc = a.scores + b0;
+  if (a.scores_copy != nullptr && a.scores_copy != a.scores)
+    for (int g = tid; g < nb; g += kToppThreads) a.scores_copy[b0 + g] = sc[g];
+
+  // largest usable score -> binary exponent e, shift = 52 - ceil(log2 nb) - e
+  uint32_t mxb = 0;
+  for (int g = tid; g < nb; g += kToppThreads) {
+    const uint32_t b = __float_as_uint(sc[g]);
+    if (usable(b) && b > mxb) mxb = b;
+  }
+  mxb = block_reduce<uint32_t>(mxb, red32, true);
+  int e = 0;
+  if (mxb != 0u) (void)frexp((double)__uint_as_float(mxb), &e);
+  const int nbits = (nb <= 1) ? 0 : 32 - __clz(nb - 1);
+  const int shift = 52 - nbits - e;
+
+  auto mass = [&](float x) -> unsigned long long {
+    return usable(__float_as_uint(x)) ? (unsigned long long)ldexp((double)x, shift) : 0ull;
+  };
+  auto key = [&](float x, int g) -> unsigned long long {
+    return ((unsigned long long)phi_bits(x) << 32) | (unsigned long long)(uint32_t)g;
+  };
+
+  unsigned long long tot = 0;
+  for (int g = tid; g < nb; g += kToppThreads) tot += mass(sc[g]);
+  tot = block_reduce<unsigned long long>(tot, red64, false);
+  const double thr = a.p * (double)tot;
+
+  // weighted radix select, 8 bits per pass from the most significant digit
+  unsigned long long prefix = 0, above = 0, pivot = 0;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int sh = 56 - 8 * pass;
+    for (int d = tid; d < 256; d += kToppThreads) { h_mass[d] = 0ull; h_cnt[d] = 0u; }
+    __syncthreads();
+    for (int g = tid; g < nb; g += kToppThreads) {
+      const float x = sc[g];
+      const unsigned long long k = key(x, g);
+      if (pass == 0 || (k >> (sh + 8)) == prefix) {
+        const int d = (int)((k >> sh) & 255ull);
+        atomicAdd(&h_mass[d], mass(x));
+        atomicAdd(&h_cnt[d], 1u);
+      }
+    }
+    __syncthreads();
+    if (wid == 0) {
+      // lane L covers digits 255-4L .. 252-4L, i.e. descending key order
+      unsigned long long m[4];
+      uint32_t cn[4];
+      unsigned long long loc = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 255 - 4 * lane - i;
+        m[i] = h_mass[d];
+        cn[i] = h_cnt[d];
+        loc += m[i];
+      }
+      unsigned long long incl = loc;
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long x = __shfl_up(incl, o);
+        if (lane >= o) incl += x;
+      }
+      unsigned long long run = above + (incl - loc);
+      int first = -1;
+      unsigned long long abv = 0;
+      uint32_t cfirst = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned long long before = run;
+        run += m[i];
+        if (first < 0 && cn[i] > 0u && (double)run >= thr) { first = i; abv = before; cfirst = cn[i]; }
+      }
+      const unsigned long long bal = __ballot(first >= 0);
+      const int sel = bal ? (__ffsll((long long)bal) - 1) : 63;
+      if (lane == sel) {
+        if (first < 0) { first = 3; abv = run - m[3]; cfirst = cn[3]; }  // unreachable: total >= thr
+        s_dsel = 255 - 4 * lane - first;
+        s_above = abv;
+        s_cnt = cfirst;
+      }
+    }
+    __syncthreads();
+    prefix = (prefix << 8) | (unsigned long long)s_dsel;
+    above = s_above;
+    if (s_cnt == 1u || pass == 7) {
+      // the group holds a single key (or all 64 bits are fixed): find it
+      if (pass == 7) {
+        pivot = prefix;
+      } else {
+        for (int g = tid; g < nb; g += kToppThreads) {
+          const unsigned long long k = key(sc[g], g);
+          if ((k >> sh) == prefix) s_key = k;
+        }
+        __syncthreads();
+        pivot = s_key;
+      }
+      break;
+    }
+  }
+
+  // keep flags and the closed-form token count of the expanded mask
+  const int A = a.A, n = a.n, G = a.G;
+  const int w0 = max(max(N - n, 0), A);
+  unsigned long long cnt = 0;
+  for (int g = tid; g < nb; g += kToppThreads) {
+    const bool kp = key(sc[g], g) >= pivot;
+    a.keep_block[b0 + g] = kp ? 1 : 0;
+    const int lo = g * G, hi = min(N, lo + G);
+    int c;
+    if (kp) {
+      c = hi - lo;
+    } else {
+      c = max(0, min(hi, A) - lo) + max(0, hi - max(lo, w0));
+    }
+    cnt += (unsigned long long)c;
+  }
+  cnt = block_reduce<unsigned long long>(cnt, red64, false);
+  if (tid == 0) a.kept[r] = (int32_t)cnt;
+}
+
+// token mask: M_i = keep[block(i)] or i < A or i >= N - n   (request-relative i)
+__global__ __launch_bounds__(256) void expand_kernel(Offsets off, int R, int G, int A, int n,
+                                                     const uint8_t* __restrict__ keep_block,
+                                                     uint8_t* __restrict__ mask, int64_t max_tokens) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= max_tokens) return;
+  const int T = off.cu[R];
+  if (i >= T || i < off.cu[0]) return;
+  const int r = find_owner(off.cu, R, i);
+  const int s = off.cu[r];
+  const int N = off.cu[r + 1] - s;
+  const int li = (int)(i - s);
+  const bool m = keep_block[off.blk[r] + li / G] != 0 || li < A || li >= N - n;
+  mask[i] = m ? 1 : 0;
+}
+
+hipError_t launch_topp(const ToppArgs& a, hipStream_t s) {
+  if (a.R > 0) {
+    hipLaunchKernelGGL(topp_kernel, dim3((unsigned)a.R), dim3(kToppThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.max_tokens > 0) {
+    hipLaunchKernelGGL(expand_kernel, dim3((unsigned)((a.max_tokens + 255) / 256)), dim3(256), 0, s,
+                       a.off, (int)a.R, (int)a.G, (int)a.A, (int)a.n, a.keep_block, a.mask, a.max_tokens);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace up
