@@ -35,7 +35,8 @@ class HipEvents:
     them on the stream its kernels run on)."""
 
     def __init__(self):
-        self.hip = ctypes.CDLL("libamdhip64.so")
+        # by soname, so the runtime torch (and the library) already loaded is reused
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]

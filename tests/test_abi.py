@@ -166,3 +166,14 @@ def test_python_binding_raises():
         call = tlb.select_blocks(p(head_dim=96), FAKE, 1, FAKE, 1, FAKE, 1, 1, None, None, None, None,
                                  FAKE, FAKE, FAKE, workspace_bytes=1, stream=0)
         del call
+
+
+def test_single_hip_runtime_in_process():
+    """The binding loads torch before libuniprefill, so the process holds one
+    HIP runtime and one HSA runtime (torch bundles its own copies under the
+    same sonames as the ROCm install)."""
+    maps = open("/proc/self/maps").read()
+    hip = set(re.findall(r"(/\S*libamdhip64\S*)", maps))
+    hsa = set(re.findall(r"(/\S*libhsa-runtime64\S*)", maps))
+    assert len(hip) == 1, hip
+    assert len(hsa) <= 1, hsa

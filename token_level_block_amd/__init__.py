@@ -18,6 +18,12 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libuniprefill.so")
 
+# One HIP runtime per process: torch ships its own libamdhip64.so.7 and HSA
+# runtime, with the same sonames as the ROCm install this library links
+# against.  Loading torch first makes libuniprefill bind to the runtime torch
+# already uses; loading it first would put two runtimes in the process.
+import torch  # noqa: E402,F401
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing; build it with `python -m token_level_block_amd.build` "
