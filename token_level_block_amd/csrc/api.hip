@@ -206,6 +206,7 @@ size_t up_compact_workspace_bytes(int32_t num_reqs, int64_t max_tokens) {
   size_t off = align_up(sizeof(int32_t) * (size_t)(num_reqs + 1));
   off = align_up(off + sizeof(int32_t) * (size_t)ntiles);
   off = align_up(off + sizeof(int32_t) * (size_t)(ntiles + 1));
+  off = align_up(off + sizeof(int32_t) * (size_t)max_tokens);
   return off;
 }
 
@@ -243,6 +244,8 @@ up_status up_compact(const uint8_t* keep_mask, const int32_t* cu_seqlens, int32_
   a.tile_count = reinterpret_cast<int32_t*>(ws + off);
   off = align_up(off + sizeof(int32_t) * (size_t)ntiles);
   a.tile_prefix = reinterpret_cast<int32_t*>(ws + off);
+  off = align_up(off + sizeof(int32_t) * (size_t)(ntiles + 1));
+  a.src_pos = reinterpret_cast<int32_t*>(ws + off);
   a.num_count_tiles = ntiles;
   a.mask = keep_mask;
   a.cu_in = cu_seqlens;

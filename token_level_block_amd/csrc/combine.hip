@@ -62,33 +62,62 @@ hipError_t launch_prep(const int32_t* cu_in, int32_t R, int64_t max_tokens, int3
 
 // ---------------------------------------------------------------------------
 // row normalisers: LSE[r][row] = log2 sum over the request's chunks
+// one workgroup = 64 rows (one per lane) x 4 waves striding over the chunks
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void row_lse_kernel(Offsets off, int R, int rows, int n,
-                                                      const float* __restrict__ chunk_lse,
-                                                      float* __restrict__ row_lse) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)R * rows) return;
-  const int r = (int)(idx / rows);
-  const int row = (int)(idx - (int64_t)r * rows);
-  const int t = row % n;
+// online merge of a log2-domain term v into (m, s) = (running max, sum 2^(x-m))
+__device__ __forceinline__ void lse_merge(float& m, float& s, float v) {
+  const float mn = fmaxf(m, v);
+  if (mn == -INFINITY) return;
+  s = s * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(v - mn);
+  m = mn;
+}
+
+__device__ __forceinline__ void lse_merge_pair(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * __builtin_amdgcn_exp2f(m - mn) + s2 * __builtin_amdgcn_exp2f(m2 - mn);
+  m = mn;
+}
+
+constexpr int kRowWaves = 4;
+
+__global__ __launch_bounds__(kRowWaves * kWave) void row_lse_kernel(Offsets off, int R, int rows, int n,
+                                                                    const float* __restrict__ chunk_lse,
+                                                                    float* __restrict__ row_lse) {
+  __shared__ float pm[kRowWaves][kWave], ps[kRowWaves][kWave];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = blockIdx.y;
+  const int row = blockIdx.x * kWave + lane;
   const int N = off.cu[r + 1] - off.cu[r];
   const int ne = min(n, N);
-  float res = -INFINITY;
-  if (t < ne) {
+  const bool valid = row < rows && (row % n) < ne;
+  float m = -INFINITY, sum = 0.f;
+  if (valid) {
     const int c0 = off.chunk[r], c1 = off.chunk[r + 1];
-    float m = -INFINITY;
-    for (int c = c0; c < c1; ++c) m = fmaxf(m, chunk_lse[(int64_t)c * rows + row]);
-    float sum = 0.f;
-    for (int c = c0; c < c1; ++c) sum += __builtin_amdgcn_exp2f(chunk_lse[(int64_t)c * rows + row] - m);
-    res = m + __log2f(sum);
+    int c = c0 + w;
+    for (; c + 3 * kRowWaves < c1; c += 4 * kRowWaves) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = chunk_lse[(int64_t)(c + u * kRowWaves) * rows + row];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lse_merge(m, sum, v[u]);
+    }
+    for (; c < c1; c += kRowWaves) lse_merge(m, sum, chunk_lse[(int64_t)c * rows + row]);
   }
-  row_lse[idx] = res;
+  pm[w][lane] = m;
+  ps[w][lane] = sum;
+  __syncthreads();
+  if (w == 0 && row < rows) {
+    for (int u = 1; u < kRowWaves; ++u) lse_merge_pair(m, sum, pm[u][lane], ps[u][lane]);
+    row_lse[(int64_t)r * rows + row] = valid ? m + __log2f(sum) : -INFINITY;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// block scores: one wave per block
+// block scores: one wave per block, 16-byte loads along the rows
 // ---------------------------------------------------------------------------
 constexpr int kSumWaves = 4;
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kSumWaves * kWave) void block_sum_kernel(
     Offsets off, int R, int rows, int n, int G, const float* __restrict__ lse,
@@ -103,20 +132,32 @@ __global__ __launch_bounds__(kSumWaves * kWave) void block_sum_kernel(
   const int ne = min(n, N);
   const float* src = lse + gb * rows;
   const float* rl = row_lse + (int64_t)r * rows;
-  float acc = 0.f;
-  for (int row = lane; row < rows; row += kWave) {
-    if (row % n < ne) acc += __builtin_amdgcn_exp2f(src[row] - rl[row]);
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  if (ne == n && (rows & 3) == 0) {
+    // every window row is valid: 4 rows per lane per step
+    for (int row = 4 * lane; row < rows; row += 4 * kWave) {
+      const floatx4 v = *reinterpret_cast<const floatx4*>(src + row);
+      const floatx4 l = *reinterpret_cast<const floatx4*>(rl + row);
+      acc0 += __builtin_amdgcn_exp2f(v[0] - l[0]);
+      acc1 += __builtin_amdgcn_exp2f(v[1] - l[1]);
+      acc2 += __builtin_amdgcn_exp2f(v[2] - l[2]);
+      acc3 += __builtin_amdgcn_exp2f(v[3] - l[3]);
+    }
+  } else {
+    for (int row = lane; row < rows; row += kWave)
+      if (row % n < ne) acc0 += __builtin_amdgcn_exp2f(src[row] - rl[row]);
   }
+  float acc = (acc0 + acc1) + (acc2 + acc3);
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
   if (lane == 0) scores[gb] = acc / ((float)G * (float)ne);
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const int rows = a.hq * a.n;
-  const int64_t nthreads = (int64_t)a.R * rows;
-  if (nthreads > 0) {
-    hipLaunchKernelGGL(row_lse_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, s,
-                       a.off, (int)a.R, rows, (int)a.n, a.chunk_lse, a.row_lse);
+  if (a.R > 0) {
+    hipLaunchKernelGGL(row_lse_kernel, dim3((unsigned)((rows + kWave - 1) / kWave), (unsigned)a.R),
+                       dim3(kRowWaves * kWave), 0, s, a.off, (int)a.R, rows, (int)a.n, a.chunk_lse,
+                       a.row_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -5,11 +5,12 @@
 //   count  : one workgroup per 4096-token tile counts the set mask bytes;
 //   scan   : one workgroup clamps cu_seqlens and turns the tile counts into
 //            exclusive prefixes;
-//   gather : one workgroup per 256-token tile ranks its kept tokens (wave
-//            ballots), writes the index map and the new request offsets that
-//            fall in its tile, and copies the kept rows of every buffer with
-//            coalesced 16-byte accesses;
-//   scatter: every compacted row goes back to its original position.
+//   rank   : one workgroup per 256-token tile ranks its kept tokens (wave
+//            ballots) and writes the index map, the stream position of every
+//            kept row and the new request offsets that fall in its tile;
+//   copy   : waves spread evenly over the kept rows copy each row of every
+//            buffer with coalesced 16-byte accesses (the same kernel moves the
+//            rows back for the Eq. 8 scatter).
 // No atomics and no inter-workgroup waiting: every result is deterministic.
 #include "common.h"
 
@@ -18,8 +19,6 @@ namespace up {
 constexpr int kCountThreads = kCountTile / 16;   // 16 mask bytes per thread
 constexpr int kGatherThreads = kGatherTile;      // one token per thread
 constexpr int kScanThreads = 1024;
-constexpr int kScatterThreads = 256;
-constexpr int kScatterRows = 16;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -38,27 +37,6 @@ __device__ __forceinline__ int count_piece(const uint8_t* mask, int64_t pos, int
   int c = 0;
   for (int64_t i = pos; i < limit; ++i) c += mask[i] != 0;
   return c;
-}
-
-// One wave copies one row: 16-byte pieces, eight loads in flight per lane.
-__device__ __forceinline__ void copy_row_vec(const uint8_t* __restrict__ sp, uint8_t* __restrict__ dp,
-                                             int cpr, int lane) {
-  int part = lane;
-  for (; part + 7 * kWave < cpr; part += 8 * kWave) {
-    u32x4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const u32x4*>(sp + (int64_t)(part + u * kWave) * 16);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) *reinterpret_cast<u32x4*>(dp + (int64_t)(part + u * kWave) * 16) = v[u];
-  }
-  for (; part < cpr; part += kWave)
-    *reinterpret_cast<u32x4*>(dp + (int64_t)part * 16) = *reinterpret_cast<const u32x4*>(sp + (int64_t)part * 16);
-}
-
-__device__ __forceinline__ void copy_row_words(const uint8_t* __restrict__ sp, uint8_t* __restrict__ dp,
-                                               int wpr, int lane) {
-  for (int part = lane; part < wpr; part += kWave)
-    *reinterpret_cast<uint32_t*>(dp + (int64_t)part * 4) = *reinterpret_cast<const uint32_t*>(sp + (int64_t)part * 4);
 }
 
 __global__ __launch_bounds__(kCountThreads) void count_kernel(const uint8_t* __restrict__ mask,
@@ -116,11 +94,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
     for (int e = tid; e <= R; e += kScanThreads) cu_out[e] = 0;
 }
 
-__global__ __launch_bounds__(kGatherThreads) void gather_kernel(CompactArgs a) {
+__global__ __launch_bounds__(kGatherThreads) void rank_kernel(CompactArgs a) {
   __shared__ int32_t red[kGatherThreads / kWave];
   __shared__ int32_t wsum[kGatherThreads / kWave];
   __shared__ int32_t excl[kGatherThreads + 1];
-  __shared__ int32_t list[kGatherThreads];
   __shared__ int32_t s_prefix;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -130,7 +107,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(CompactArgs a) {
   const int64_t end = min<int64_t>(start + kGatherTile, T);
 
   // kept tokens before this tile: the count tile's prefix plus the pieces of
-  // the count tile that precede this gather tile
+  // the count tile that precede this tile
   const int64_t ct = start / kCountTile;
   const int64_t cstart = ct * kCountTile;
   int c = 0;
@@ -147,7 +124,6 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(CompactArgs a) {
     s_prefix = t;
   }
 
-  // rank the kept tokens of this tile
   const int64_t i = start + tid;
   const bool kept = (i < end) && a.mask[i] != 0;
   const unsigned long long bal = __ballot(kept);
@@ -159,34 +135,86 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(CompactArgs a) {
   const int local = wpre + below;
   excl[tid] = local;
   if (tid == kGatherThreads - 1) excl[kGatherThreads] = local + (kept ? 1 : 0);
-  if (kept) list[local] = tid;
   __syncthreads();
   const int32_t prefix = s_prefix;
-  const int cnt = excl[kGatherThreads];
 
-  if (kept) a.index_out[prefix + local] = a.index_in ? a.index_in[i] : (int32_t)i;
-
+  if (kept) {
+    a.index_out[prefix + local] = a.index_in ? a.index_in[i] : (int32_t)i;
+    a.src_pos[prefix + local] = (int32_t)i;
+  }
   // new request offsets that fall inside this tile (the last tile also owns position T)
   for (int r = tid; r <= a.R; r += kGatherThreads) {
     const int32_t p = a.cu_s[r];
     if (p >= start && (p < end || (p == T && end == T)))
       a.cu_out[r] = prefix + excl[p - start];
   }
+}
 
-  // copy kept rows of every buffer, one wave per row
-  constexpr int nw = kGatherThreads / kWave;
-  for (int b = 0; b < a.bufs.nbuf; ++b) {
-    const uint8_t* src = a.bufs.src[b];
-    uint8_t* dst = a.bufs.dst[b];
-    const int64_t rb = a.bufs.row_bytes[b];
-    const bool vec = a.bufs.vec16[b] != 0;
-    for (int row = wid; row < cnt; row += nw) {
-      const uint8_t* sp = src + (start + list[row]) * rb;
-      uint8_t* dp = dst + (int64_t)(prefix + row) * rb;
-      if (vec) copy_row_vec(sp, dp, (int)(rb >> 4), lane);
-      else copy_row_words(sp, dp, (int)(rb >> 2), lane);
+// ---------------------------------------------------------------------------
+// Row copy over the kept rows k < count:  kGather: dst row k <- src row map[k]
+//                                         scatter: dst row map[k] <- src row k
+// Rows are dealt round-robin to waves; a wave moves one row at a time with up
+// to eight 16-byte nontemporal loads in flight per lane (the rows are streamed
+// once, so they bypass cache residency).
+// ---------------------------------------------------------------------------
+constexpr int kCopyThreads = 256;
+constexpr int kCopyWaves = kCopyThreads / kWave;
+
+template <bool kGather, bool kVec>
+__global__ __launch_bounds__(kCopyThreads) void copy_rows_kernel(const uint8_t* __restrict__ src,
+                                                                 uint8_t* __restrict__ dst, int64_t rb,
+                                                                 const int32_t* __restrict__ map,
+                                                                 const int32_t* __restrict__ count_ptr,
+                                                                 int64_t max_rows, int64_t dst_rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * kCopyWaves + (threadIdx.x >> 6);
+  const int64_t W = (int64_t)gridDim.x * kCopyWaves;
+  const int64_t count = min<int64_t>(*count_ptr, max_rows);
+  for (int64_t k = gw; k < count; k += W) {
+    const int64_t s = kGather ? (int64_t)map[k] : k;
+    const int64_t d = kGather ? k : (int64_t)map[k];
+    if (d < 0 || d >= dst_rows) continue;
+    if (kVec) {
+      const u32x4* sp = reinterpret_cast<const u32x4*>(src + s * rb);
+      u32x4* dp = reinterpret_cast<u32x4*>(dst + d * rb);
+      const int units = (int)(rb >> 4);
+      int u = lane;
+      for (; u + 7 * kWave < units; u += 8 * kWave) {
+        u32x4 v[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) v[x] = __builtin_nontemporal_load(sp + u + x * kWave);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) __builtin_nontemporal_store(v[x], dp + u + x * kWave);
+      }
+      for (; u < units; u += kWave) __builtin_nontemporal_store(__builtin_nontemporal_load(sp + u), dp + u);
+    } else {
+      const uint32_t* sp = reinterpret_cast<const uint32_t*>(src + s * rb);
+      uint32_t* dp = reinterpret_cast<uint32_t*>(dst + d * rb);
+      const int units = (int)(rb >> 2);
+      for (int u = lane; u < units; u += kWave) dp[u] = sp[u];
     }
   }
+}
+
+static unsigned copy_grid(int64_t max_rows) {
+  // enough waves to fill the chip (256 CUs x 32 waves), fewer for small batches
+  const int64_t want = (max_rows + kCopyWaves - 1) / kCopyWaves;
+  return (unsigned)(want < 1 ? 1 : (want > 2048 ? 2048 : want));
+}
+
+static hipError_t launch_copy(bool gather, bool vec, const uint8_t* src, uint8_t* dst, int64_t rb,
+                              const int32_t* map, const int32_t* count_ptr, int64_t max_rows,
+                              int64_t dst_rows, hipStream_t s) {
+  const dim3 grid(copy_grid(max_rows)), block(kCopyThreads);
+  if (gather && vec)
+    hipLaunchKernelGGL((copy_rows_kernel<true, true>), grid, block, 0, s, src, dst, rb, map, count_ptr, max_rows, dst_rows);
+  else if (gather)
+    hipLaunchKernelGGL((copy_rows_kernel<true, false>), grid, block, 0, s, src, dst, rb, map, count_ptr, max_rows, dst_rows);
+  else if (vec)
+    hipLaunchKernelGGL((copy_rows_kernel<false, true>), grid, block, 0, s, src, dst, rb, map, count_ptr, max_rows, dst_rows);
+  else
+    hipLaunchKernelGGL((copy_rows_kernel<false, false>), grid, block, 0, s, src, dst, rb, map, count_ptr, max_rows, dst_rows);
+  return hipGetLastError();
 }
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
@@ -202,52 +230,28 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int64_t ntiles = (a.max_tokens + kGatherTile - 1) / kGatherTile;
   if (ntiles > 0) {
-    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)ntiles), dim3(kGatherThreads), 0, s, a);
+    hipLaunchKernelGGL(rank_kernel, dim3((unsigned)ntiles), dim3(kGatherThreads), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  for (int b = 0; b < a.bufs.nbuf; ++b) {
+    e = launch_copy(true, a.bufs.vec16[b] != 0, a.bufs.src[b], a.bufs.dst[b], a.bufs.row_bytes[b], a.src_pos,
+                    a.cu_out + a.R, a.max_tokens, a.max_tokens, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
 // Eq. 8 carry-forward: full[index_map[k]] = compacted[k], k < count
 // ---------------------------------------------------------------------------
-template <bool kVec>
-__global__ __launch_bounds__(kScatterThreads) void scatter_kernel(const uint8_t* __restrict__ src,
-                                                                  int64_t rb,
-                                                                  const int32_t* __restrict__ index_map,
-                                                                  const int32_t* __restrict__ count_ptr,
-                                                                  uint8_t* __restrict__ full,
-                                                                  int64_t full_rows, int64_t max_rows) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int64_t k0 = (int64_t)blockIdx.x * kScatterRows;
-  const int64_t count = min<int64_t>(*count_ptr, max_rows);
-  if (k0 >= count) return;
-  const int nrows = (int)min<int64_t>(kScatterRows, count - k0);
-  constexpr int nw = kScatterThreads / kWave;
-  for (int row = wid; row < nrows; row += nw) {
-    const int32_t d = index_map[k0 + row];
-    if (d < 0 || d >= full_rows) continue;
-    const uint8_t* sp = src + (k0 + row) * rb;
-    uint8_t* dp = full + (int64_t)d * rb;
-    if (kVec) copy_row_vec(sp, dp, (int)(rb >> 4), lane);
-    else copy_row_words(sp, dp, (int)(rb >> 2), lane);
-  }
-}
-
 hipError_t launch_scatter(const void* compacted, int64_t row_bytes, const int32_t* index_map,
                           const int32_t* count_ptr, int64_t max_tokens, void* full,
                           int64_t full_rows, hipStream_t s) {
-  const int64_t nblk = (max_tokens + kScatterRows - 1) / kScatterRows;
-  if (nblk <= 0) return hipSuccess;
+  if (max_tokens <= 0) return hipSuccess;
   const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)compacted % 16 == 0) && ((uintptr_t)full % 16 == 0);
-  if (vec)
-    hipLaunchKernelGGL(scatter_kernel<true>, dim3((unsigned)nblk), dim3(kScatterThreads), 0, s,
-                       (const uint8_t*)compacted, row_bytes, index_map, count_ptr, (uint8_t*)full, full_rows,
-                       max_tokens);
-  else
-    hipLaunchKernelGGL(scatter_kernel<false>, dim3((unsigned)nblk), dim3(kScatterThreads), 0, s,
-                       (const uint8_t*)compacted, row_bytes, index_map, count_ptr, (uint8_t*)full, full_rows,
-                       max_tokens);
-  return hipGetLastError();
+  return launch_copy(false, vec, static_cast<const uint8_t*>(compacted), static_cast<uint8_t*>(full), row_bytes,
+                     index_map, count_ptr, max_tokens, full_rows, s);
 }
 
 }  // namespace up

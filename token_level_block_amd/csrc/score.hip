@@ -4,12 +4,17 @@
 //
 // One workgroup owns (request, chunk of keys, KV head, slice of queries).  The
 // window queries of every query head that shares the KV head (GQA) are held in
-// registers as the B operand of v_mfma_f32_32x32x16_bf16; 32-key tiles of K
-// are staged through LDS (double buffered) as the A operand, so each 32x32
-// accumulator tile has keys on rows and queries on columns and each lane owns
-// one query column.  Per 32-key tile a lane keeps a running maximum and a
-// rescaled sum of 2^(c z) over the keys of the current G-block (c = softmax
-// scale * log2 e); at each block end it emits the log2-domain partial
+// registers as the B operand of v_mfma_f32_32x32x16_bf16.  K streams through
+// a double-buffered LDS ring with gfx950's direct global-to-LDS 16-byte loads
+// (no staging registers, XOR-swizzled rows so the A-operand reads are free of
+// bank conflicts) and feeds the A operand, so each 32x32 accumulator tile has
+// keys on rows and queries on columns and each lane owns one query column.  Each lane keeps, per query column, a reference logit
+// (the running maximum so far, raised only when needed) and sums 2^(c(z-ref))
+// over the keys of the current G-block (c = softmax scale * log2 e).  A tile
+// whose per-lane partial sum exceeds 2^20 (or is not finite) is redone with
+// its exact maximum as the new reference, so every term stays within fp32
+// range; the common case needs no per-logit max.  At each block end a lane
+// emits the log2-domain partial
 //     lse[g][row] = log2 sum_{i in block g} 2^(c z_i)
 // and folds it into a per-chunk partial.  The logits never reach memory.
 // Keys after a window row's own position are masked (causal masking), as
@@ -22,24 +27,68 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int D>
+template <int D, int NW>
 struct ScoreCfg {
-  static constexpr int KSTEPS = D / 16;        // MFMA k-steps per 32-key tile
-  static constexpr int NT = 2;                 // 32-query column tiles per wave
-  static constexpr int QW = 32 * NT;           // queries per wave
-  static constexpr int KT = (D <= 128) ? 64 : 32;   // keys per LDS stage
-  static constexpr int ROWB = D * 2 + 16;      // padded LDS bytes per key row
-  static constexpr int STAGE = KT * ROWB;      // bytes per LDS stage
-  static constexpr int CHUNKS = KT * D / 8;    // 16-byte pieces per stage
-  static constexpr int MIN_THREADS = 256;
-  static constexpr int MAXC = (CHUNKS + MIN_THREADS - 1) / MIN_THREADS;  // pieces per thread
+  static constexpr int KSTEPS = D / 16;              // MFMA k-steps per 32-key tile
+  static constexpr int NT = 2;                       // 32-query column tiles per wave
+  static constexpr int QW = 32 * NT;                 // queries per wave
+  static constexpr int KT = (D <= 128) ? 128 : 64;   // keys per LDS stage
+  static constexpr int SUB = KT / 32;                // 32-key tiles per stage
+  static constexpr int ROWB = D * 2;                 // bytes per key row in LDS (no padding)
+  static constexpr int PPR = D / 8;                  // 16-byte pieces per key row
+  static constexpr int SWZ = PPR < 16 ? PPR - 1 : 15;   // piece p of key r sits in slot p ^ (r & SWZ)
+  static constexpr int STAGE = KT * ROWB;            // bytes per LDS stage
+  static constexpr int KPI = 1024 / ROWB;            // keys per 1 KB wave load
+  static constexpr int NPW = STAGE / 1024 / NW;      // 1 KB wave loads per wave per stage
+  static_assert(STAGE % (1024 * NW) == 0, "a stage must split evenly into 1 KB wave loads");
 };
 
-__device__ __forceinline__ float wave_swap_half(float v) { return __shfl_xor(v, 32); }
+// s_waitcnt vmcnt(0) with the other counters left free (gfx9 encoding)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
-template <int D>
-__global__ __launch_bounds__(512) void score_kernel(ScoreArgs a) {
-  using C = ScoreCfg<D>;
+// value of the lane 32 positions away (the other half of the same query column)
+__device__ __forceinline__ float other_half(float v) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  // each lane now holds {v[l], v[l ^ 32]} in some order
+  const float a = __uint_as_float(pr[0]), b = __uint_as_float(pr[1]);
+  return (__lane_id() < 32) ? b : a;
+}
+
+__device__ __forceinline__ float half_max(float v) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+
+__device__ __forceinline__ float half_sum(float v) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+}
+
+// sum over this lane's 16 logits of 2^(c z + nrc), nrc = -c * ref
+__device__ __forceinline__ float tile_sum(const floatx16& acc, float cl2, float nrc) {
+  float s0 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[0], cl2, nrc));
+  float s1 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[1], cl2, nrc));
+  float s2 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[2], cl2, nrc));
+  float s3 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[3], cl2, nrc));
+#pragma unroll
+  for (int e = 4; e < 16; e += 4) {
+    s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e + 0], cl2, nrc));
+    s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e + 1], cl2, nrc));
+    s2 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e + 2], cl2, nrc));
+    s3 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e + 3], cl2, nrc));
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
+// Largest tile partial accepted without rescaling; keeps every term of the
+// block sums far from fp32 overflow.
+constexpr float kRescaleAbove = 1048576.0f;   // 2^20
+
+// GT = G/32 tiles per block when G is 32, 64 or 128 (block ends known at
+// compile time in the plain stages), 0 for any other multiple of 32.
+template <int D, int NW, int GT>
+__global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
+  using C = ScoreCfg<D, NW>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
 
   const int gc = blockIdx.x;
@@ -58,8 +107,7 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreArgs a) {
   const int gq = a.hq / a.hkv;
   const int rows = a.hq * n;
   const int qn = gq * n;                    // queries that read KV head j
-  const int nthreads = blockDim.x;
-  const int nwaves = nthreads >> 6;
+  constexpr int nwaves = NW;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5;
   const int gblk0 = a.off.blk[r];
@@ -86,109 +134,147 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreArgs a) {
     }
   }
 
-  // ---- K staging: global -> registers -> LDS ----
+  // ---- K staging: direct global -> LDS loads (16 bytes per lane) ----
+  // wave load c of a stage fills LDS bytes [c KB, c KB + 1 KB): keys KPI*c + lane/PPR,
+  // slot lane%PPR, which holds piece slot ^ (key & SWZ) of that key (XOR swizzle)
+  const int lkey = lane / C::PPR, lslot = lane % C::PPR;
   const uint16_t* kbase = a.k + (int64_t)s * a.k_stride + (int64_t)j * D;
-  u32x4 pre[C::MAXC];
-  auto load_stage = [&](int kb) {
+  auto load_stage = [&](int kb, int buf) {
 #pragma unroll
-    for (int i = 0; i < C::MAXC; ++i) {
-      const int ch = tid + i * nthreads;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ch < C::CHUNKS) {
-        const int key = ch / (D / 8), part = ch - (ch / (D / 8)) * (D / 8);
-        if (kb + key < k1)
-          v = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(kb + key) * a.k_stride + part * 8);
-      }
-      pre[i] = v;
-    }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::MAXC; ++i) {
-      const int ch = tid + i * nthreads;
-      if (ch < C::CHUNKS) {
-        const int key = ch / (D / 8), part = ch - (ch / (D / 8)) * (D / 8);
-        *reinterpret_cast<u32x4*>(smem + buf * C::STAGE + key * C::ROWB + part * 16) = pre[i];
-      }
+    for (int i = 0; i < C::NPW; ++i) {
+      const int cidx = wid * C::NPW + i;
+      const int key = C::KPI * cidx + lkey;
+      const int p = lslot ^ (key & C::SWZ);
+      const int gk = min(kb + key, k1 - 1);   // rows past the chunk end re-read a valid row; they are masked
+      const uint16_t* g = kbase + (int64_t)gk * a.k_stride + p * 8;
+      __builtin_amdgcn_global_load_lds((const void*)g,
+          (__attribute__((address_space(3))) void*)(smem + buf * C::STAGE + cidx * 1024), 16, 0, 0);
     }
   };
 
-  // ---- running softmax state per query column ----
-  const float cl2 = a.c;
-  float mb[C::NT], eb[C::NT], cm[C::NT], ce[C::NT];
+  // A-fragment reads: key row ks*32 + (lane&31), pieces kk*2 + half (swizzled)
+  const int arow = lane & 31;
+  const int aswz = arow & C::SWZ;   // (ks*32 + arow) & SWZ == arow & SWZ since SWZ < 32
+  auto mfma_tile = [&](const uint8_t* sbuf, int ks, floatx16 (&acc)[C::NT]) {
+    const uint8_t* rowp = sbuf + (ks * 32 + arow) * C::ROWB;
 #pragma unroll
-  for (int nt = 0; nt < C::NT; ++nt) { mb[nt] = -INFINITY; eb[nt] = 0.f; cm[nt] = -INFINITY; ce[nt] = 0.f; }
+    for (int kk = 0; kk < C::KSTEPS; ++kk) {
+      const int slot = (kk * 2 + half) ^ aswz;
+      const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(rowp + (slot << 4)));
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[nt][kk], kk == 0 ? floatx16{} : acc[nt], 0, 0, 0);
+    }
+  };
+
+  // ---- softmax state per query column ----
+  const float cl2 = a.c;
+  float ref[C::NT], nrc[C::NT], eb[C::NT], cm[C::NT], ce[C::NT];
+#pragma unroll
+  for (int nt = 0; nt < C::NT; ++nt) {
+    ref[nt] = -INFINITY; nrc[nt] = INFINITY; eb[nt] = 0.f; cm[nt] = -INFINITY; ce[nt] = 0.f;
+  }
+
+  // rare: raise the reference to the exact running maximum and redo the tile
+  auto rescale = [&](floatx16 (&acc)[C::NT], float (&ts)[C::NT]) {
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      float mx = fmaxf(fmaxf(acc[nt][0], acc[nt][1]), acc[nt][2]);
+#pragma unroll
+      for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, acc[nt][e]), acc[nt][e + 1]);
+      mx = fmaxf(mx, acc[nt][15]);
+      const float mnew = fmaxf(ref[nt], half_max(mx));
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      eb[nt] *= __builtin_amdgcn_exp2f((ref[nt] - muse) * cl2);
+      ref[nt] = mnew;
+      nrc[nt] = -muse * cl2;
+      ts[nt] = tile_sum(acc[nt], cl2, nrc[nt]);
+    }
+  };
+  // block gi is complete: emit its partial and fold it into the chunk partial
+  auto flush = [&](int gi) {
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      const float E = half_sum(eb[nt]);
+      const float l = (ref[nt] == -INFINITY) ? -INFINITY : ref[nt] * cl2 + __log2f(E);
+      if (half == 0 && qrow[nt] >= 0) a.lse[(int64_t)(gblk0 + gi) * rows + qrow[nt]] = l;
+      const float cnew = fmaxf(cm[nt], l);
+      const float cuse = (cnew == -INFINITY) ? 0.f : cnew;
+      ce[nt] = ce[nt] * __builtin_amdgcn_exp2f(cm[nt] - cuse) + __builtin_amdgcn_exp2f(l - cuse);
+      cm[nt] = cnew;
+      eb[nt] = 0.f;
+    }
+  };
+  // general tile: causal / tail masking, any block size
+  auto process = [&](floatx16 (&acc)[C::NT], int kt) {
+    // accumulator element e of this lane holds key kt + 8*(e/4) + 4*half + (e%4)
+    if (kt + 32 > N - ne) {
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kt + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (key > qlim[nt]) acc[nt][e] = -INFINITY;
+        }
+    }
+    float ts[C::NT];
+    bool bad = false;
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      ts[nt] = tile_sum(acc[nt], cl2, nrc[nt]);
+      bad |= !(ts[nt] <= kRescaleAbove);
+    }
+    if (__any(bad)) rescale(acc, ts);
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) eb[nt] += ts[nt];
+    // block end: the next tile starts a new G-block, or the chunk ends here
+    if (((kt + 32) % G == 0) || (kt + 32 >= k1)) flush(kt / G);
+  };
 
   const int nstages = (k1 - k0 + C::KT - 1) / C::KT;
-  load_stage(k0);
-  store_stage(0);
+  load_stage(k0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
+  floatx16 acc[C::NT];
   for (int st = 0; st < nstages; ++st) {
     const int kb = k0 + st * C::KT;
-    if (st + 1 < nstages) load_stage(kb + C::KT);
+    // the next stage lands in the other buffer while this one is consumed
+    if (st + 1 < nstages) load_stage(kb + C::KT, (st + 1) & 1);
     const uint8_t* sbuf = smem + (st & 1) * C::STAGE;
-
+    const bool plain = (kb + C::KT <= k1) && (kb + C::KT <= N - ne);
+    if (GT > 0 && plain) {
+      // every tile full and unmasked; block ends at fixed tiles
 #pragma unroll
-    for (int ks = 0; ks < C::KT / 32; ++ks) {
-      const int kt = kb + ks * 32;          // first key of this tile (request-relative)
-      if (kt < k1) {
-        floatx16 acc[C::NT];
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) acc[nt] = floatx16{};
-        const uint8_t* arow = sbuf + (ks * 32 + (lane & 31)) * C::ROWB + half * 16;
-#pragma unroll
-        for (int kk = 0; kk < C::KSTEPS; ++kk) {
-          const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow + kk * 32));
-#pragma unroll
-          for (int nt = 0; nt < C::NT; ++nt)
-            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[nt][kk], acc[nt], 0, 0, 0);
-        }
-        // accumulator element e of this lane holds key kt + 8*(e/4) + 4*half + (e%4)
-        const bool edge = (kt + 32 > N - ne);
+      for (int ks = 0; ks < C::SUB; ++ks) {
+        mfma_tile(sbuf, ks, acc);
+        float ts[C::NT];
+        bool bad = false;
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
-          if (edge) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int key = kt + 8 * (e >> 2) + 4 * half + (e & 3);
-              if (key > qlim[nt]) acc[nt][e] = -INFINITY;
-            }
-          }
-          float mx = acc[nt][0];
-#pragma unroll
-          for (int e = 1; e < 16; ++e) mx = fmaxf(mx, acc[nt][e]);
-          mx = fmaxf(mx, wave_swap_half(mx));
-          const float mnew = fmaxf(mb[nt], mx);
-          const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-          const float alpha = __builtin_amdgcn_exp2f((mb[nt] - muse) * cl2);
-          const float nmc = -muse * cl2;
-          float sum = 0.f;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[nt][e], cl2, nmc));
-          eb[nt] = eb[nt] * alpha + sum;
-          mb[nt] = mnew;
+          ts[nt] = tile_sum(acc[nt], cl2, nrc[nt]);
+          bad |= !(ts[nt] <= kRescaleAbove);
         }
-        // block end: the next tile starts a new G-block, or the chunk ends here
-        const bool bend = ((kt + 32) % G == 0) || (kt + 32 >= k1);
-        if (bend) {
-          const int gi = kt / G;
+        if (__any(bad)) rescale(acc, ts);
 #pragma unroll
-          for (int nt = 0; nt < C::NT; ++nt) {
-            const float E = eb[nt] + wave_swap_half(eb[nt]);
-            const float l = (mb[nt] == -INFINITY) ? -INFINITY : mb[nt] * cl2 + __log2f(E);
-            if (half == 0 && qrow[nt] >= 0) a.lse[(int64_t)(gblk0 + gi) * rows + qrow[nt]] = l;
-            const float cnew = fmaxf(cm[nt], l);
-            const float cuse = (cnew == -INFINITY) ? 0.f : cnew;
-            ce[nt] = ce[nt] * __builtin_amdgcn_exp2f(cm[nt] - cuse) + __builtin_amdgcn_exp2f(l - cuse);
-            cm[nt] = cnew;
-            mb[nt] = -INFINITY;
-            eb[nt] = 0.f;
-          }
+        for (int nt = 0; nt < C::NT; ++nt) eb[nt] += ts[nt];
+        if constexpr (GT > 0 && GT <= C::SUB) {
+          if ((ks + 1) % GT == 0) flush((kb + ks * 32) / G);
+        } else if constexpr (GT > 0) {
+          if (ks + 1 == C::SUB && ((kb + C::KT) % G) == 0) flush((kb + ks * 32) / G);
+        }
+      }
+    } else {
+      const int nsub = min(C::SUB, (k1 - kb + 31) / 32);   // 32-key tiles holding keys < k1
+#pragma unroll
+      for (int ks = 0; ks < C::SUB; ++ks) {
+        if (ks < nsub) {
+          mfma_tile(sbuf, ks, acc);
+          process(acc, kb + ks * 32);
         }
       }
     }
-    if (st + 1 < nstages) store_stage((st + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's loads of the next stage have landed
     __syncthreads();
   }
 
@@ -201,17 +287,30 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreArgs a) {
   }
 }
 
+template <int D, int GT>
+static hipError_t launch_score_dg(const ScoreArgs& a, hipStream_t s) {
+  // 4 waves when the KV head's window queries fit in 256 columns, else 8 waves
+  // and as many query slices (grid z) as needed
+  const int qn = (a.hq / a.hkv) * a.n;
+  if (qn <= 4 * 64) {
+    dim3 grid((unsigned)a.max_chunks, (unsigned)a.hkv, 1u);
+    hipLaunchKernelGGL((score_kernel<D, 4, GT>), grid, dim3(4 * kWave), 0, s, a);
+  } else {
+    const int zsplit = (qn + 8 * 64 - 1) / (8 * 64);
+    dim3 grid((unsigned)a.max_chunks, (unsigned)a.hkv, (unsigned)zsplit);
+    hipLaunchKernelGGL((score_kernel<D, 8, GT>), grid, dim3(8 * kWave), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_score_d(const ScoreArgs& a, hipStream_t s) {
-  using C = ScoreCfg<D>;
-  const int qn = (a.hq / a.hkv) * a.n;
-  int nwaves = (qn + C::QW - 1) / C::QW;
-  if (nwaves < C::MIN_THREADS / kWave) nwaves = C::MIN_THREADS / kWave;
-  if (nwaves > 8) nwaves = 8;
-  const int zsplit = (qn + nwaves * C::QW - 1) / (nwaves * C::QW);
-  dim3 grid((unsigned)a.max_chunks, (unsigned)a.hkv, (unsigned)zsplit);
-  hipLaunchKernelGGL(score_kernel<D>, grid, dim3(nwaves * kWave), 0, s, a);
-  return hipGetLastError();
+  switch (a.G) {
+    case 32: return launch_score_dg<D, 1>(a, s);
+    case 64: return launch_score_dg<D, 2>(a, s);
+    case 128: return launch_score_dg<D, 4>(a, s);
+    default: return launch_score_dg<D, 0>(a, s);
+  }
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s) {

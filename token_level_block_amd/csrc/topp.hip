@@ -16,6 +16,7 @@ namespace up {
 
 constexpr int kToppThreads = 512;
 constexpr int kToppWaves = kToppThreads / kWave;
+constexpr int kToppCache = 4096;   // requests with at most this many blocks keep their keys in LDS
 
 __device__ __forceinline__ uint32_t phi_bits(float x) {
   const uint32_t b = __float_as_uint(x);
@@ -41,6 +42,7 @@ __device__ __forceinline__ T block_reduce(T v, T* red, bool is_max) {
 }
 
 __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
+  __shared__ unsigned long long s_keys[kToppCache];
   __shared__ unsigned long long h_mass[256];
   __shared__ uint32_t h_cnt[256];
   __shared__ unsigned long long red64[kToppWaves];
@@ -80,10 +82,21 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
   auto key = [&](float x, int g) -> unsigned long long {
     return ((unsigned long long)phi_bits(x) << 32) | (unsigned long long)(uint32_t)g;
   };
+  // the score back from the high half of a packed key (phi is invertible)
+  auto score_of = [](unsigned long long k) -> float {
+    const uint32_t ph = (uint32_t)(k >> 32);
+    return __uint_as_float((ph & 0x80000000u) ? (ph ^ 0x80000000u) : ~ph);
+  };
+  const bool cached = nb <= kToppCache;
+  auto key_at = [&](int g) -> unsigned long long { return cached ? s_keys[g] : key(sc[g], g); };
 
   unsigned long long tot = 0;
-  for (int g = tid; g < nb; g += kToppThreads) tot += mass(sc[g]);
-  tot = block_reduce<unsigned long long>(tot, red64, false);
+  for (int g = tid; g < nb; g += kToppThreads) {
+    const float x = sc[g];
+    if (cached) s_keys[g] = key(x, g);
+    tot += mass(x);
+  }
+  tot = block_reduce<unsigned long long>(tot, red64, false);   // (its barriers also publish s_keys)
   const double thr = a.p * (double)tot;
 
   // weighted radix select, 8 bits per pass from the most significant digit
@@ -93,11 +106,10 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
     for (int d = tid; d < 256; d += kToppThreads) { h_mass[d] = 0ull; h_cnt[d] = 0u; }
     __syncthreads();
     for (int g = tid; g < nb; g += kToppThreads) {
-      const float x = sc[g];
-      const unsigned long long k = key(x, g);
+      const unsigned long long k = key_at(g);
       if (pass == 0 || (k >> (sh + 8)) == prefix) {
         const int d = (int)((k >> sh) & 255ull);
-        atomicAdd(&h_mass[d], mass(x));
+        atomicAdd(&h_mass[d], mass(score_of(k)));
         atomicAdd(&h_cnt[d], 1u);
       }
     }
@@ -147,7 +159,7 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
         pivot = prefix;
       } else {
         for (int g = tid; g < nb; g += kToppThreads) {
-          const unsigned long long k = key(sc[g], g);
+          const unsigned long long k = key_at(g);
           if ((k >> sh) == prefix) s_key = k;
         }
         __syncthreads();
@@ -162,7 +174,7 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
   const int w0 = max(max(N - n, 0), A);
   unsigned long long cnt = 0;
   for (int g = tid; g < nb; g += kToppThreads) {
-    const bool kp = key(sc[g], g) >= pivot;
+    const bool kp = key_at(g) >= pivot;
     a.keep_block[b0 + g] = kp ? 1 : 0;
     const int lo = g * G, hi = min(N, lo + G);
     int c;
