@@ -83,6 +83,25 @@ def cpu_oracle_step(wl, cu, q, k, hidden_host):
     return dt, sel
 
 
+def measured_traffic(root):
+    """HBM bytes per score-kernel launch from the committed counter summary, or
+    None when score.hip has changed since the counters were taken."""
+    import hashlib
+    import re
+    prof = os.path.join(root, "profiles", "score_kernel_llama8b_128k_hbm.md")
+    src = os.path.join(root, "token_level_block_amd", "csrc", "score.hip")
+    try:
+        text = open(prof).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    h = re.search(r"score.hip sha256 at measurement: `([0-9a-f]+)`", text)
+    if not m or not h or h.group(1) != sha:
+        return None
+    return int(m.group(1))
+
+
 def threads_used():
     n = len(os.sched_getaffinity(0))
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
@@ -98,6 +117,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures the single-GPU hot path only; --gpus {args.gpus} is not supported "
@@ -115,6 +136,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.int32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {src.numel() * 4} bytes three times")
+        return
 
     wl = synth.llama_128k()
     log(f"[bench] generating {wl.name}: lengths={wl.lengths} hq={wl.hq} hkv={wl.hkv} d={wl.d} D={wl.hidden}")
@@ -226,7 +256,7 @@ def main():
                    "n": wl.n, "p": wl.p, "keep_ratio": round(keep_ratio, 4)},
         "roofline": {"bound": "mfma", "kernel": "score_kernel<128>", "achieved": score_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": score_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)))},
         "roofline_compact": {"bound": "hbm", "kernel": "up_compact", "achieved": compact_gbs,
                              "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": compact_gbs / PEAK_HBM_GBS},
         "roofline_scatter": {"bound": "hbm", "kernel": "up_scatter_back", "achieved": scatter_gbs,
