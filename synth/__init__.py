@@ -240,8 +240,14 @@ def hidden_words(rows: np.ndarray, nwords: int) -> np.ndarray:
 def hidden_words_torch(row0: int, nrows: int, nwords: int, device):
     """Same pattern as hidden_words for rows [row0, row0+nrows), as a torch int32 tensor."""
     import torch
-    i = torch.arange(row0, row0 + nrows, dtype=torch.int64, device=device)[:, None]
-    j = torch.arange(nwords, dtype=torch.int64, device=device)[None, :]
+    return hidden_words_torch_at(torch.arange(row0, row0 + nrows, dtype=torch.int64, device=device), nwords)
+
+
+def hidden_words_torch_at(rows, nwords: int):
+    """Same pattern as hidden_words for the rows listed in a torch tensor."""
+    import torch
+    i = rows.to(torch.int64)[:, None]
+    j = torch.arange(nwords, dtype=torch.int64, device=rows.device)[None, :]
     v = (i * _MI + j * _MJ + _C0) & 0xFFFFFFFF
     v = torch.where(v >= 2 ** 31, v - 2 ** 32, v)
     return v.to(torch.int32)
@@ -293,6 +299,16 @@ def serving_16x128k(seed: int = 4, lengths=None, layer: int = 0) -> Workload:
         structs.append(RequestStructure("hot", hot=h, hot_lambda=8.0))
     return Workload(f"llama8b_16x128k_layer{layer}", tuple(int(x) for x in lengths),
                     seed=seed + 1000 * layer, structures=tuple(structs), **LLAMA_8B)
+
+
+def serving_16x128k_layer1_lengths(seed: int = 4) -> tuple:
+    """Lengths of the second selection's stream: the tokens of the hot blocks the
+    first layer's generator planted plus the two sink and two window blocks."""
+    wl0 = serving_16x128k(seed)
+    out = []
+    for N, st in zip(wl0.lengths, wl0.structures):
+        out.append(int(min(N, (st.hot + 4) * STRUCT_BLOCK)))
+    return tuple(out)
 
 
 def tiny(lengths, hq=4, hkv=2, d=64, hidden=64, G=8, A=8, n=8, p=0.9, seed=0,

@@ -331,3 +331,123 @@ def test_llama_128k_end_to_end():
     assert torch.equal(full[keep], hidden[keep] + 1)
     say(f"  kept tokens={int(got['kept'][0])} ({got['kept'][0] / T:.3f}) blocks kept="
         f"{int(got['keep'].sum())}/{len(got['keep'])} mismatched={mism}")
+
+
+# ---------------------------------------------------------------------------
+# serving-scale batch: 16 requests x 131072 tokens, two drop layers
+# ---------------------------------------------------------------------------
+def _upload_hidden(T, nwords):
+    hid = torch.empty((T, nwords), dtype=torch.int32, device="cuda")
+    step = 1 << 16
+    for a in range(0, T, step):
+        z = min(T, a + step)
+        hid[a:z] = synth.hidden_words_torch(a, z - a, nwords, "cuda")
+    return hid
+
+
+def _serving_layer(wl, sample):
+    cu, q, k = synth.make_qk(wl)
+    say(f"  generated {wl.name}: T={int(cu[-1])}")
+    got = run_select(wl, cu, q, k)
+    offs = got["offs"]
+    b = got["b"].astype(np.float64)
+    keep = got["keep"].astype(bool)
+    mask = got["mask"]
+    for r in range(wl.num_reqs):
+        a, z = int(offs[r]), int(offs[r + 1])
+        N = int(cu[r + 1] - cu[r])
+        ne = min(wl.n, N)
+        # every window row's softmax sums to one: sum_g b_g G n_eff = Hq n_eff
+        assert abs(b[a:z].sum() * wl.G * ne - wl.hq * ne) <= 1e-4 * wl.hq * ne, r
+        # Eq. 6 (aggregated) for the GPU's own selection
+        tot = b[a:z].sum()
+        assert b[a:z][~keep[a:z]].sum() <= (1 - wl.p) * tot * (1 + 1e-6), r
+        i = np.arange(N)
+        want = (keep[a:z][i // wl.G] | (i < wl.A) | (i >= N - wl.n)).astype(np.uint8)
+        assert np.array_equal(mask[cu[r]:cu[r + 1]], want), r
+        assert int(got["kept"][r]) == int(want.sum()), r
+    for r in sample:
+        s0, N = int(cu[r]), int(cu[r + 1] - cu[r])
+        b_ref, _ = oracle.request_block_scores(q, k, s0, N, wl.hq, wl.hkv, wl.d, wl.G, wl.n)
+        a, z = int(offs[r]), int(offs[r + 1])
+        check_scores(got["b"][a:z], b_ref, np.array([0, z - a]))
+        b32 = b_ref.astype(np.float32)
+        keep_ref = oracle.top_p_select(b32, wl.p)
+        diff = np.nonzero(keep_ref != keep[a:z])[0]
+        if len(diff):
+            from gpu_helpers import allowed_mismatch
+            ok = allowed_mismatch(b32, keep_ref, wl.p)
+            assert ok[diff].all(), (r, diff[:10])
+        say(f"  request {r}: oracle agrees, kept {int(got['kept'][r])}/{N}, mismatched blocks {len(diff)}")
+    return cu, got
+
+
+@pytest.mark.timeout(1200)
+def test_serving_16x128k_two_layers():
+    """Two selections in a row on 16 x 131072 packed tokens: scores of two sampled
+    requests per layer against the oracle, invariants for all 16, the 16 GiB
+    hidden-row compaction and Eq. 8 scatter by formula, and the drop history of
+    both layers."""
+    wl0 = synth.serving_16x128k(layer=0)
+    R = wl0.num_reqs
+    cu0, got0 = _serving_layer(wl0, sample=(0, 9))
+    T0 = int(cu0[-1])
+    nwords = wl0.hidden // 2
+    hidden = _upload_hidden(T0, nwords)
+    out = torch.empty_like(hidden)
+    cb = CompactBuffers.allocate(R, T0)
+    cb.run(got0["bufs"].keep_mask, dev(cu0), [hidden], [out])
+    torch.cuda.synchronize()
+    cu_out0 = cb.cu_out.cpu().numpy()
+    K = int(cu_out0[-1])
+    assert np.array_equal(np.diff(cu_out0), got0["kept"])
+    idx = cb.index_out[:K]
+    assert bool((idx[1:] > idx[:-1]).all())
+    assert torch.equal(torch.nonzero(got0["bufs"].keep_mask[:T0]).flatten().to(torch.int32), idx)
+    step = 1 << 16
+    for a in range(0, K, step):
+        z = min(K, a + step)
+        assert torch.equal(out[a:z], synth.hidden_words_torch_at(idx[a:z], nwords)), a
+    # Eq. 8 with processed = compacted + 1
+    out[:K] += 1
+    run_scatter_back(out, cb.index_out, cb.cu_out, R, T0, hidden)
+    torch.cuda.synchronize()
+    keepm = got0["bufs"].keep_mask[:T0] != 0
+    for a in range(0, T0, step):
+        z = min(T0, a + step)
+        ref = synth.hidden_words_torch(a, z - a, nwords, "cuda")
+        m = keepm[a:z]
+        assert torch.equal(hidden[a:z][m], ref[m] + 1), a
+        assert torch.equal(hidden[a:z][~m], ref[~m]), a
+    del hidden, out
+    torch.cuda.empty_cache()
+
+    # second selection on a compacted stream of generator-defined lengths
+    L = 32
+    mb = MetadataBuffers.allocate(np.diff(cu0), L, 4)
+    mb.run(3, dev(cu0), cb.cu_out)
+    wl1 = synth.serving_16x128k(lengths=synth.serving_16x128k_layer1_lengths(), layer=1)
+    cu1, got1 = _serving_layer(wl1, sample=(4, 13))
+    cb1 = CompactBuffers.allocate(R, int(cu1[-1]))
+    zero = torch.zeros((int(cu1[-1]), 4), dtype=torch.int32, device="cuda")
+    cb1.run(got1["bufs"].keep_mask, dev(cu1), [zero], [torch.empty_like(zero)])
+    mb.run(11, dev(cu1), cb1.cu_out)
+    torch.cuda.synchronize()
+    kept0 = got0["kept"].astype(np.int64)
+    kept1 = got1["kept"].astype(np.int64)
+    orig = np.diff(cu0).astype(np.int64)
+    s_after0 = kept0
+    s_after1 = kept0 - (np.diff(cu1) - kept1)
+    assert np.array_equal(mb.seq_lens.cpu().numpy(), s_after1)
+    assert np.array_equal(mb.drop_count.cpu().numpy(), np.full(R, 2))
+    dl = mb.drop_layer.cpu().numpy().reshape(R, 4)
+    dn = mb.drop_len.cpu().numpy().reshape(R, 4)
+    assert (dl[:, 0] == 3).all() and (dl[:, 1] == 11).all()
+    assert np.array_equal(dn[:, 0], s_after0) and np.array_equal(dn[:, 1], s_after1)
+    # Eq. 17 table: original length up to the first drop layer, then the
+    # retained length after the last drop at a strictly earlier layer
+    base = mb.seqused_base.cpu().numpy().reshape(L, R)
+    for lp in range(L):
+        want = orig if lp <= 3 else (s_after0 if lp <= 11 else s_after1)
+        assert np.array_equal(base[lp], want), lp
+    say(f"  layer0 kept {int(kept0.sum())}/{T0}, layer1 kept {int(kept1.sum())}/{int(cu1[-1])}")
