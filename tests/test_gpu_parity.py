@@ -451,3 +451,15 @@ def test_serving_16x128k_two_layers():
         want = orig if lp <= 3 else (s_after0 if lp <= 11 else s_after1)
         assert np.array_equal(base[lp], want), lp
     say(f"  layer0 kept {int(kept0.sum())}/{T0}, layer1 kept {int(kept1.sum())}/{int(cu1[-1])}")
+
+
+# ---------------------------------------------------------------------------
+# window sizes of the paper's ablation (n = 32 and n = 512; Table 4)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [32, 512])
+def test_window_ablation_sizes(n):
+    wl = synth.with_structures(
+        synth.Workload(f"llama8b_16k_n{n}", (16384, 3000), n=n, seed=21, **synth.LLAMA_8B),
+        [synth.RequestStructure("powerlaw", c=synth.POWERLAW_C)] * 2)
+    ref, got, mism = check_select(wl)
+    say(f"  n={n}: kept={got['kept'].tolist()} mismatched={mism}")

@@ -247,7 +247,11 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
       // every tile full and unmasked; block ends at fixed tiles
 #pragma unroll
       for (int ks = 0; ks < C::SUB; ++ks) {
+        // MFMA bursts at raised wave priority: the SIMD's other wave fills the
+        // VALU while this one streams the matrix core
+        __builtin_amdgcn_s_setprio(1);
         mfma_tile(sbuf, ks, acc);
+        __builtin_amdgcn_s_setprio(0);
         float ts[C::NT];
         bool bad = false;
 #pragma unroll
