@@ -83,20 +83,31 @@ def cpu_oracle_step(wl, cu, q, k, hidden_host):
     return dt, sel
 
 
+SCORE_SOURCES = ("common.h", "api.hip", "score.hip")   # the kernel and its launch configuration
+
+
+def score_sources_sha(root):
+    import hashlib
+    h = hashlib.sha256()
+    for name in SCORE_SOURCES:
+        with open(os.path.join(root, "token_level_block_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(root):
     """HBM bytes per score-kernel launch from the committed counter summary, or
-    None when score.hip has changed since the counters were taken."""
-    import hashlib
+    None when the kernel or its launch configuration has changed since the
+    counters were taken."""
     import re
     prof = os.path.join(root, "profiles", "score_kernel_llama8b_128k_hbm.md")
-    src = os.path.join(root, "token_level_block_amd", "csrc", "score.hip")
     try:
         text = open(prof).read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = score_sources_sha(root)
     except OSError:
         return None
     m = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    h = re.search(r"score.hip sha256 at measurement: `([0-9a-f]+)`", text)
+    h = re.search(r"score kernel sources sha256 at measurement: `([0-9a-f]+)`", text)
     if not m or not h or h.group(1) != sha:
         return None
     return int(m.group(1))
