@@ -113,6 +113,46 @@ def measured_traffic(root):
     return int(m.group(1))
 
 
+def measure_peaks(stream, ev):
+    """Rates this GPU sustains, from libuppeaks: dense bf16 MFMA on random
+    operands (TFLOP/s) and a streaming 1 GiB device copy (GB/s, read + write).
+    Best of three launches after one warm-up each."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                   "token_level_block_amd", "libuppeaks.so"))
+    lib.upk_mfma_out_floats.restype = ctypes.c_int64
+    lib.upk_mfma_out_floats.argtypes = [ctypes.c_int32]
+    lib.upk_mfma_flops.restype = ctypes.c_double
+    lib.upk_mfma_flops.argtypes = [ctypes.c_int32]
+    lib.upk_mfma_launch.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    lib.upk_copy_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                    ctypes.c_void_p]
+
+    def best(launch, work):
+        rates = []
+        for i in range(4):
+            a, b = ev.new(), ev.new()
+            ev.record(a, stream)
+            if launch() != 0:
+                raise RuntimeError("peak probe launch failed")
+            ev.record(b, stream)
+            if i > 0:
+                rates.append(work / (ev.ms(a, b) * 1e-3))
+        return max(rates)
+
+    blocks = 256 * 8
+    out = torch.empty(lib.upk_mfma_out_floats(blocks), dtype=torch.float32, device="cuda")
+    mfma = best(lambda: lib.upk_mfma_launch(out.data_ptr(), blocks, stream), lib.upk_mfma_flops(blocks)) / 1e12
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    copy = best(lambda: lib.upk_copy_launch(src.data_ptr(), dst.data_ptr(), nbytes, 256 * 16, stream),
+                2.0 * nbytes) / 1e9
+    torch.cuda.synchronize()
+    del out, src, dst
+    return mfma, copy
+
+
 def threads_used():
     n = len(os.sched_getaffinity(0))
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
@@ -237,6 +277,15 @@ def main():
     scatter_gbs = scatter_bytes / (scatter_ms * 1e-3) / 1e9
     log(f"[bench] {ms_per_step:.3f} ms/step  select {select_ms:.3f} (score {score_ms:.3f}) compact "
         f"{compact_ms:.3f} metadata {meta_ms:.3f} scatter {scatter_ms:.3f}  kept {kept}/{T}")
+    # select + compact as HBM work (the score GEMM's K reads are counted under MFMA):
+    # kept rows read and written, index map, token mask, block scores and flags
+    nblocks = int(sel.block_offsets[R].item())
+    sc_bytes = 2 * kept * row_bytes + 4 * kept + T + 5 * nblocks
+    sc_gbs = sc_bytes / ((select_ms + compact_ms) * 1e-3) / 1e9
+    del qd, kd, hidden, out, full
+    torch.cuda.empty_cache()
+    mfma_peak, copy_peak = measure_peaks(stream, ev)
+    log(f"[bench] measured peaks: bf16 MFMA {mfma_peak:.0f} TFLOP/s (random operands), copy {copy_peak:.0f} GB/s")
     ev.close()
 
     cpu = None
@@ -267,11 +316,20 @@ def main():
                    "n": wl.n, "p": wl.p, "keep_ratio": round(keep_ratio, 4)},
         "roofline": {"bound": "mfma", "kernel": "score_kernel<128>", "achieved": score_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": score_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)))},
+                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),
+                     "measured_peak": mfma_peak, "frac_measured": score_tflops / mfma_peak},
         "roofline_compact": {"bound": "hbm", "kernel": "up_compact", "achieved": compact_gbs,
-                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": compact_gbs / PEAK_HBM_GBS},
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": compact_gbs / PEAK_HBM_GBS,
+                             "measured_peak": copy_peak, "frac_measured": compact_gbs / copy_peak},
         "roofline_scatter": {"bound": "hbm", "kernel": "up_scatter_back", "achieved": scatter_gbs,
-                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": scatter_gbs / PEAK_HBM_GBS},
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": scatter_gbs / PEAK_HBM_GBS,
+                             "measured_peak": copy_peak, "frac_measured": scatter_gbs / copy_peak},
+        "hbm_select_compact": {"achieved": sc_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": sc_gbs / PEAK_HBM_GBS, "measured_peak": copy_peak,
+                               "frac_measured": sc_gbs / copy_peak},
+        "measured_peaks": {"bf16_mfma_tflops": mfma_peak, "copy_gbs": copy_peak,
+                           "how": "libuppeaks: random-operand 32x32x16 bf16 MFMA loop at 2 waves/SIMD; "
+                                  "1 GiB streaming copy, read + write bytes"},
         "breakdown_ms": {"select": select_ms, "score_kernel": score_ms, "compact": compact_ms,
                          "metadata": meta_ms, "scatter_back": scatter_ms},
         "select_compact_tokens_per_s": sel_compact_tps,

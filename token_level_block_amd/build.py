@@ -3,8 +3,9 @@
     python -m token_level_block_amd.build        # or: python token_level_block_amd/build.py
 
 Every .hip file under csrc/ is compiled to an object in _build/ and linked
-into token_level_block_amd/libuniprefill.so.  Packed fp32 instructions are
-disabled for all device code.
+into token_level_block_amd/libuniprefill.so.  peaks/peaks.hip (reference
+MFMA and copy rates, loaded only by the benchmark) becomes libuppeaks.so.
+Packed fp32 instructions are disabled for all device code.
 """
 from __future__ import annotations
 
@@ -19,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libuniprefill.so")
+PEAKS_SRC = os.path.join(PKG, "peaks", "peaks.hip")
+PEAKS_LIB = os.path.join(PKG, "libuppeaks.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -60,20 +63,26 @@ def build(verbose: bool = True) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        results = list(ex.map(lambda s: _compile(hipcc, s), srcs))
+    with ThreadPoolExecutor(min(8, len(srcs) + 1)) as ex:
+        results = list(ex.map(lambda s: _compile(hipcc, s), srcs + [PEAKS_SRC]))
     for obj, warn in results:
         if warn.strip() and verbose:
             print(warn, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]]
+    objs = [o for o, _ in results]
+    _link(hipcc, objs[:-1], LIB)
+    _link(hipcc, objs[-1:], PEAKS_LIB)
+    if verbose:
+        print(f"built {LIB} and {PEAKS_LIB}")
+    return LIB
+
+
+def _link(hipcc, objs, out):
+    tmp = out + ".tmp"
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{p.stdout}\n{p.stderr}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
-    return LIB
+    os.replace(tmp, out)
 
 
 if __name__ == "__main__":
