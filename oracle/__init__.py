@@ -25,4 +25,7 @@ from .uniprefill_oracle import (  # noqa: F401
     update_metadata,
     seqused_eq17,
     MetadataState,
+    retained_positions,
+    slot_mapping,
+    write_kv_cache,
 )

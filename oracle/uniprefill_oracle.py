@@ -267,3 +267,63 @@ def seqused_eq17(history_r, layer_prime: int, orig_len: int, kv_len: int) -> int
     before = [(l, s) for (l, s) in history_r if l < layer_prime]
     base = max(before)[1] if before else orig_len
     return int(base + (kv_len - orig_len))
+
+
+# ---------------------------------------------------------------------------
+# Per-layer KV cache slots and the paged-cache write: UniPrefill Sec. 3.5
+# ("vLLM scheduler integration"), Eq. 16
+# ---------------------------------------------------------------------------
+def retained_positions(cu_seqlens, seq_lens):
+    """Logical position p_i of every row of the (compacted) token stream.
+
+    Reading of p_i in Eq. 16: a layer after a drop caches only the retained
+    tokens, densely (its KV length is the retained length, Eq. 17), so the
+    k-th retained token of request r sits at p = (seq_lens[r] - kept_r) + k,
+    where seq_lens[r] - kept_r counts the request's tokens already cached
+    before this prefill chunk (zero for a fresh prefill).  seq_lens are the
+    patched lengths after the drop."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    sl = np.asarray(seq_lens, dtype=np.int64)
+    pos = np.empty(int(cu[-1]), dtype=np.int64)
+    for r in range(len(cu) - 1):
+        kept = int(cu[r + 1] - cu[r])
+        pos[cu[r]: cu[r + 1]] = (sl[r] - kept) + np.arange(kept)
+    return pos
+
+
+def slot_mapping(block_table, B: int, cu_seqlens, seq_lens, max_tokens=None):
+    """Eq. 16: slot_i = block_table[r_i, floor(p_i / B)] * B + (p_i mod B).
+
+    One slot per row of the stream, padded with -1 up to max_tokens.  A row
+    whose position falls outside the table (p < 0, or floor(p / B) beyond the
+    table's width) or whose table entry is negative gets -1: no slot."""
+    table = np.asarray(block_table, dtype=np.int64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T = int(cu[-1])
+    width = table.shape[1] if table.ndim == 2 else 0
+    slots = np.full(T if max_tokens is None else int(max_tokens), -1, dtype=np.int64)
+    pos = retained_positions(cu, seq_lens)
+    for r in range(len(cu) - 1):
+        for i in range(int(cu[r]), int(cu[r + 1])):
+            p = int(pos[i])
+            if p < 0 or p // B >= width:
+                continue
+            phys = int(table[r, p // B])
+            if phys >= 0:
+                slots[i] = phys * B + p % B
+    return slots
+
+
+def write_kv_cache(key_cache, value_cache, slots, key, value, count: int):
+    """Rows i < count of key and value go to cache row slots[i] (slot-major
+    cache: [num_blocks * B, row]); rows without a slot (negative, or past the
+    cache) are not written.  Returns the new caches."""
+    kc = np.array(key_cache, copy=True)
+    vc = None if value_cache is None else np.array(value_cache, copy=True)
+    for i in range(int(count)):
+        s = int(slots[i])
+        if 0 <= s < len(kc):
+            kc[s] = key[i]
+            if vc is not None:
+                vc[s] = value[i]
+    return kc, vc

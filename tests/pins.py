@@ -375,4 +375,103 @@ def check_metadata_conservation(impl):
 COMPACT_CHECKS = [check_compact_roundtrip, check_compact_composition,
                   check_eq17_fixture, check_metadata_conservation]
 
-ALL_CHECKS = SCORE_CHECKS + TOPP_CHECKS + COMPACT_CHECKS
+
+# ---------------------------------------------------------------------------
+# Per-layer KV cache slots (Eq. 16) and the paged-cache write
+# ---------------------------------------------------------------------------
+def check_slot_fixture(impl):
+    g = load_golden("eq16_slot_example.json")
+    pos = impl.retained_positions(g["cu_seqlens"], g["seq_lens"])
+    assert list(pos) == g["positions"]
+    s = impl.slot_mapping(g["block_table"], g["B"], g["cu_seqlens"], g["seq_lens"], g["max_tokens"])
+    assert list(s) == g["slots"], list(s)
+
+
+def _random_slot_case(rng, R, B, width, contiguous):
+    kept = rng.integers(0, 3 * B + 5, size=R)
+    ctx = rng.integers(0, 2 * B + 3, size=R)
+    cu = np.concatenate([[0], np.cumsum(kept)]).astype(np.int64)
+    seq = ctx + kept
+    if contiguous:
+        base = rng.integers(0, 1000, size=R)
+        table = base[:, None] + np.arange(width)[None, :]
+    else:
+        table = rng.permutation(R * width).reshape(R, width)
+    return kept, ctx, cu, seq, table
+
+
+def check_slot_closed_form(impl):
+    """With a contiguous table row (entries base_r, base_r + 1, ...), block
+    column times B plus the offset inside the block is just p: the slot is
+    base_r * B + p."""
+    rng = np.random.default_rng(21)
+    for B in (1, 3, 4, 16):
+        kept, ctx, cu, seq, table = _random_slot_case(rng, 5, B, width=64, contiguous=True)
+        s = impl.slot_mapping(table, B, cu, seq)
+        for r in range(5):
+            p = ctx[r] + np.arange(kept[r])
+            assert np.array_equal(s[cu[r]: cu[r + 1]], table[r, 0] * B + p)
+
+
+def check_slot_structure(impl):
+    """Disjoint tables: valid slots are distinct, sit in the table's block for
+    column floor(p/B) at offset p mod B, and exactly the positions past the
+    table's width get -1."""
+    rng = np.random.default_rng(22)
+    for B, width in ((4, 3), (5, 6), (16, 2)):
+        kept, ctx, cu, seq, table = _random_slot_case(rng, 6, B, width, contiguous=False)
+        s = impl.slot_mapping(table, B, cu, seq, int(cu[-1]) + 7)
+        assert np.all(s[int(cu[-1]):] == -1)
+        valid = s[s >= 0]
+        assert len(np.unique(valid)) == len(valid)
+        for r in range(6):
+            p = ctx[r] + np.arange(kept[r])
+            sr = s[cu[r]: cu[r + 1]]
+            inside = p // B < width
+            assert np.array_equal(sr >= 0, inside)
+            assert np.array_equal(sr[inside] % B, p[inside] % B)
+            assert np.array_equal(sr[inside] // B, table[r, p[inside] // B])
+
+
+def check_slot_eq17_consistency(impl):
+    """After a drop, the positions a later layer writes are exactly the
+    seqused of Eq. 17 entries of its cache (the tokens cached before this
+    chunk, then the retained ones): Eq. 16 and Eq. 17 agree."""
+    rng = np.random.default_rng(23)
+    lens = rng.integers(1, 90, size=5)
+    prior = rng.integers(0, 40, size=5)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    mask = (rng.random(int(cu[-1])) < 0.5).astype(np.uint8)
+    _, _, cu_out = impl.compact(mask, cu)
+    st = impl.MetadataState.fresh(lens + prior)
+    st, _ = impl.update_metadata(st, 6, cu, cu_out)
+    pos = impl.retained_positions(cu_out, st.seq_lens)
+    for r in range(5):
+        used = impl.seqused_eq17(st.history[r], 7, int(lens[r] + prior[r]), int(lens[r] + prior[r]))
+        pr = pos[cu_out[r]: cu_out[r + 1]]
+        assert np.array_equal(pr, np.arange(prior[r], used))
+
+
+def check_kv_write(impl):
+    """Every row with a slot lands in that cache row, rows past `count` and
+    rows without a slot write nothing, and every other cache row keeps its
+    value."""
+    rng = np.random.default_rng(24)
+    rows, width, nslots = 40, 6, 64
+    key = rng.integers(0, 2 ** 31, size=(rows, width), dtype=np.int64)
+    val = key + 7
+    slots = rng.permutation(nslots + 20)[:rows] - 10        # some negative, some past the cache
+    kc0 = np.full((nslots, width), -5, dtype=np.int64)
+    kc, vc = impl.write_kv_cache(kc0, kc0 - 1, slots, key, val, count=33)
+    hit = np.zeros(nslots, bool)
+    for i in range(33):
+        if 0 <= slots[i] < nslots:
+            assert np.array_equal(kc[slots[i]], key[i]) and np.array_equal(vc[slots[i]], val[i])
+            hit[slots[i]] = True
+    assert np.all(kc[~hit] == -5) and np.all(vc[~hit] == -6)
+
+
+SLOT_CHECKS = [check_slot_fixture, check_slot_closed_form, check_slot_structure,
+               check_slot_eq17_consistency, check_kv_write]
+
+ALL_CHECKS = SCORE_CHECKS + TOPP_CHECKS + COMPACT_CHECKS + SLOT_CHECKS

@@ -165,6 +165,40 @@ def _scatter_all(full, compacted, index_map, count):
     return out
 
 
+def _slot_variant(positions="dense", swap_div_mod=False):
+    def retained_positions(cu_seqlens, seq_lens):
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        sl = np.asarray(seq_lens, dtype=np.int64)
+        pos = np.empty(int(cu[-1]), dtype=np.int64)
+        for r in range(len(cu) - 1):
+            kept = int(cu[r + 1] - cu[r])
+            ctx = {"dense": sl[r] - kept, "no_context": 0, "context_plus_one": sl[r] - kept + 1}[positions]
+            pos[cu[r]: cu[r + 1]] = ctx + np.arange(kept)
+        return pos
+
+    def slot_mapping(block_table, B, cu_seqlens, seq_lens, max_tokens=None):
+        table = np.asarray(block_table, dtype=np.int64)
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        width = table.shape[1]
+        slots = np.full(int(cu[-1]) if max_tokens is None else int(max_tokens), -1, dtype=np.int64)
+        pos = retained_positions(cu, seq_lens)
+        for r in range(len(cu) - 1):
+            for i in range(int(cu[r]), int(cu[r + 1])):
+                p = int(pos[i])
+                col, off = (p % B, p // B) if swap_div_mod else (p // B, p % B)
+                if p < 0 or col >= width:
+                    continue
+                phys = int(table[r, col])
+                if phys >= 0:
+                    slots[i] = phys * B + off
+        return slots
+    return _namespace(retained_positions=retained_positions, slot_mapping=slot_mapping)
+
+
+def _kv_write_all_rows(key_cache, value_cache, slots, key, value, count):
+    return U.write_kv_cache(key_cache, value_cache, slots, key, value, len(slots))
+
+
 MUTANTS = {
     "head_mean": _scoring_mutant(ti_kw=dict(head_mean=True)),
     "no_causal_mask": _scoring_mutant(ti_kw=dict(causal=False)),
@@ -186,6 +220,10 @@ MUTANTS = {
     "eq17_le": _namespace(seqused_eq17=_seqused_le),
     "eq17_first_drop": _namespace(seqused_eq17=_seqused_first),
     "seq_lens_set_to_kept": _namespace(update_metadata=_update_sets_kept),
+    "slot_without_context": _slot_variant(positions="no_context"),
+    "slot_context_off_by_one": _slot_variant(positions="context_plus_one"),
+    "slot_div_mod_swapped": _slot_variant(swap_div_mod=True),
+    "kv_write_ignores_count": _namespace(write_kv_cache=_kv_write_all_rows),
 }
 
 
