@@ -83,7 +83,7 @@ def cpu_oracle_step(wl, cu, q, k, hidden_host):
     return dt, sel
 
 
-SCORE_SOURCES = ("common.h", "api.hip", "score.hip")   # the kernel and its launch configuration
+SCORE_SOURCES = ("score_plan.h", "score.hip")   # the kernel and the plan that sizes its launch
 
 
 def score_sources_sha(root):

@@ -190,6 +190,63 @@ up_status up_update_metadata(int32_t layer, int32_t num_layers, int32_t num_reqs
                              int32_t* drop_count, int32_t* drop_layer, int32_t* drop_len,
                              int32_t max_drops, int32_t* seqused_base, hipStream_t stream);
 
+/*
+ * up_slot_mapping - per-layer KV cache slots of the (compacted) token stream,
+ * UniPrefill Sec. 3.5 ("vLLM scheduler integration"), Eq. 16:
+ *   slot_k = block_table[r][p_k / B] * B + p_k % B
+ * for stream row k of request r, where p_k is the row's logical position.
+ * A layer after a drop caches only the retained tokens, densely after the
+ * tokens the request already had cached, so
+ *   p_k = seq_lens[r] - kept_r + (k - cu_seqlens[r]),  kept_r = cu_seqlens[r+1] - cu_seqlens[r]
+ * with seq_lens the lengths patched by up_update_metadata (p_k = rank among
+ * the retained tokens for a fresh prefill).  Each layer passes its own block
+ * table (global and sliding-window layers may differ).
+ *
+ * block_table   int32 [num_reqs][block_table_stride]; columns
+ *               [0, max_blocks_per_req) hold physical block ids (negative:
+ *               no block).  May be NULL when max_blocks_per_req is 0.
+ * kv_block_size B >= 1 tokens per physical block.
+ * cu_seqlens    int32 [num_reqs + 1], nondecreasing stream offsets (e.g. up_compact's cu_seqlens_out).
+ * seq_lens      int32 [num_reqs].
+ * slot_mapping  out int64 [max_tokens]; -1 for rows past cu_seqlens[num_reqs],
+ *               for positions p < 0 or p / B >= max_blocks_per_req, and for
+ *               negative table entries.
+ * Errors: UP_ERR_NULL, UP_ERR_SHAPE (negative sizes, stride < width,
+ * max_tokens > INT32_MAX), UP_ERR_PARAM (B < 1), UP_ERR_ALIGN (int32 arrays
+ * 4-byte, slot_mapping 8-byte aligned), UP_ERR_HIP.
+ */
+up_status up_slot_mapping(const int32_t* block_table, int64_t block_table_stride,
+                          int32_t max_blocks_per_req, int32_t kv_block_size,
+                          const int32_t* cu_seqlens, const int32_t* seq_lens, int32_t num_reqs,
+                          int64_t max_tokens, int64_t* slot_mapping, hipStream_t stream);
+
+/*
+ * up_write_kv_cache - store the retained rows' keys and values in the paged
+ * cache at the slots of Eq. 16 (UniPrefill Sec. 3.5, the physical slot
+ * mapping that lets PagedAttention read the compacted cache unchanged).
+ *
+ * For k < min(cu_seqlens[num_reqs], max_tokens) with 0 <= slot_mapping[k] < cache_slots:
+ *   key_cache row slot_mapping[k]   = key row k    (row_bytes bytes)
+ *   value_cache row slot_mapping[k] = value row k
+ * Rows without a slot are skipped; every other cache row keeps its value.
+ * Slots must not repeat (up_slot_mapping's never do for disjoint tables).
+ *
+ * key, value            rows of row_bytes bytes at strides key_row_stride /
+ *                       value_row_stride bytes (>= row_bytes; e.g. a view
+ *                       into a fused QKV projection).  value and value_cache
+ *                       are both NULL for a key-only cache.
+ * key_cache, value_cache slot-major caches [cache_slots][row_bytes], i.e. the
+ *                       [num_blocks][B][num_heads_kv][head_dim] layout.
+ * row_bytes             positive multiple of 4 (16-byte aligned rows and
+ *                       strides take the vector path).
+ * Errors: UP_ERR_NULL, UP_ERR_SHAPE, UP_ERR_PARAM, UP_ERR_ALIGN, UP_ERR_HIP.
+ */
+up_status up_write_kv_cache(const void* key, int64_t key_row_stride, const void* value,
+                            int64_t value_row_stride, int64_t row_bytes, const int64_t* slot_mapping,
+                            const int32_t* cu_seqlens, int32_t num_reqs, int64_t max_tokens,
+                            void* key_cache, void* value_cache, int64_t cache_slots,
+                            hipStream_t stream);
+
 /* Static description of a status code. */
 const char* up_status_string(up_status status);
 

@@ -201,3 +201,39 @@ def test_peaks_library_exports_and_rejects():
     assert lib.upk_copy_launch(FAKE, FAKE, 100, 4, None) == -1      # not a multiple of 16
     assert lib.upk_copy_launch(FAKE_MIS, FAKE, 64, 4, None) == -1
     assert lib.upk_copy_launch(None, FAKE, 64, 4, None) == -1
+
+
+def test_slot_mapping_and_kv_write_reject():
+    sm = lambda **kw: tlb.slot_mapping(kw.get("bt", FAKE), kw.get("bts", 8), kw.get("w", 8), kw.get("B", 16),
+                                       kw.get("cu", FAKE), kw.get("sl", FAKE), kw.get("R", 2),
+                                       kw.get("T", 100), kw.get("out", FAKE), stream=0, raise_on_error=False)
+    assert sm(cu=None) == tlb.UP_ERR_NULL
+    assert sm(sl=None) == tlb.UP_ERR_NULL
+    assert sm(out=None) == tlb.UP_ERR_NULL
+    assert sm(bt=None) == tlb.UP_ERR_NULL
+    assert sm(R=-1) == tlb.UP_ERR_SHAPE
+    assert sm(T=-1) == tlb.UP_ERR_SHAPE
+    assert sm(T=2 ** 31) == tlb.UP_ERR_SHAPE
+    assert sm(w=9) == tlb.UP_ERR_SHAPE            # wider than the row stride
+    assert sm(w=-1) == tlb.UP_ERR_SHAPE
+    assert sm(B=0) == tlb.UP_ERR_PARAM
+    assert sm(out=FAKE + 4) == tlb.UP_ERR_ALIGN   # int64 output
+    assert sm(cu=FAKE + 2) == tlb.UP_ERR_ALIGN
+    kv = lambda **kw: tlb.write_kv_cache(kw.get("k", FAKE), kw.get("ks", 2048), kw.get("v", FAKE),
+                                         kw.get("vs", 2048), kw.get("rb", 2048), kw.get("sl", FAKE),
+                                         kw.get("cu", FAKE), kw.get("R", 1), kw.get("T", 10),
+                                         kw.get("kc", FAKE), kw.get("vc", FAKE), kw.get("cs", 64),
+                                         stream=0, raise_on_error=False)
+    assert kv(k=None) == tlb.UP_ERR_NULL
+    assert kv(kc=None) == tlb.UP_ERR_NULL
+    assert kv(sl=None) == tlb.UP_ERR_NULL
+    assert kv(v=None) == tlb.UP_ERR_NULL          # value without value_cache (or the reverse)
+    assert kv(vc=None) == tlb.UP_ERR_NULL
+    assert kv(rb=6) == tlb.UP_ERR_PARAM
+    assert kv(rb=0) == tlb.UP_ERR_PARAM
+    assert kv(ks=1024) == tlb.UP_ERR_SHAPE        # stride below the row size
+    assert kv(cs=-1) == tlb.UP_ERR_SHAPE
+    assert kv(R=-1) == tlb.UP_ERR_SHAPE
+    assert kv(ks=2050) == tlb.UP_ERR_ALIGN
+    assert kv(k=FAKE + 2) == tlb.UP_ERR_ALIGN
+    assert kv(sl=FAKE + 4) == tlb.UP_ERR_ALIGN

@@ -26,7 +26,7 @@ import torch  # noqa: E402,F401
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing; build it with `python -m token_level_block_amd.build` "
+        f"{LIB_PATH} is missing; build it with `python token_level_block_amd/build.py` "
         "(hipcc, gfx950).  There is no CPU fallback.")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -42,7 +42,7 @@ UP_SCORES_IN = 1
 
 EXPORTED = ("up_max_blocks", "up_select_workspace_bytes", "up_select_blocks",
             "up_compact_workspace_bytes", "up_compact", "up_scatter_back",
-            "up_update_metadata", "up_status_string")
+            "up_update_metadata", "up_slot_mapping", "up_write_kv_cache", "up_status_string")
 
 
 class SelectParams(ctypes.Structure):
@@ -87,6 +87,10 @@ _lib.up_scatter_back.restype = ctypes.c_int
 _lib.up_scatter_back.argtypes = [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _vp]
 _lib.up_update_metadata.restype = ctypes.c_int
 _lib.up_update_metadata.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp]
+_lib.up_slot_mapping.restype = ctypes.c_int
+_lib.up_slot_mapping.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _i32, _i64, _vp, _vp]
+_lib.up_write_kv_cache.restype = ctypes.c_int
+_lib.up_write_kv_cache.argtypes = [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _vp, _i64, _vp]
 _lib.up_status_string.restype = ctypes.c_char_p
 _lib.up_status_string.argtypes = [ctypes.c_int]
 
@@ -186,3 +190,21 @@ def update_metadata(layer, num_layers, num_reqs, cu_seqlens_old, cu_seqlens_new,
                                  _ptr(drop_layer), _ptr(drop_len), max_drops, _ptr(seqused_base),
                                  _stream(stream))
     return _check(st, "up_update_metadata", raise_on_error)
+
+
+def slot_mapping(block_table, block_table_stride, max_blocks_per_req, kv_block_size, cu_seqlens, seq_lens,
+                 num_reqs, max_tokens, slots, stream=None, raise_on_error=True):
+    """up_slot_mapping (Eq. 16 per-layer KV cache slots, int64 out)."""
+    st = _lib.up_slot_mapping(_ptr(block_table), block_table_stride, max_blocks_per_req, kv_block_size,
+                              _ptr(cu_seqlens), _ptr(seq_lens), num_reqs, max_tokens, _ptr(slots),
+                              _stream(stream))
+    return _check(st, "up_slot_mapping", raise_on_error)
+
+
+def write_kv_cache(key, key_row_stride, value, value_row_stride, row_bytes, slots, cu_seqlens, num_reqs,
+                   max_tokens, key_cache, value_cache, cache_slots, stream=None, raise_on_error=True):
+    """up_write_kv_cache (retained rows into the paged cache; strides in bytes)."""
+    st = _lib.up_write_kv_cache(_ptr(key), key_row_stride, _ptr(value), value_row_stride, row_bytes,
+                                _ptr(slots), _ptr(cu_seqlens), num_reqs, max_tokens, _ptr(key_cache),
+                                _ptr(value_cache), cache_slots, _stream(stream))
+    return _check(st, "up_write_kv_cache", raise_on_error)

@@ -1,6 +1,9 @@
 """Build libuniprefill.so (gfx950 only) in-tree with hipcc.
 
-    python -m token_level_block_amd.build        # or: python token_level_block_amd/build.py
+    python token_level_block_amd/build.py
+
+(run as a script: importing the package would first load the library that
+is being rebuilt).
 
 Every .hip file under csrc/ is compiled to an object in _build/ and linked
 into token_level_block_amd/libuniprefill.so.  peaks/peaks.hip (reference

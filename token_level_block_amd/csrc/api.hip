@@ -5,6 +5,7 @@
 
 #include "../../include/uniprefill.h"
 #include "common.h"
+#include "score_plan.h"
 
 namespace {
 
@@ -13,28 +14,6 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
-
-// Keys per score workgroup.  A workgroup pays a fixed start-up (its query
-// fragments and first K stage arrive before any MFMA can issue), so chunks are
-// made as long as possible while one launch still offers about one workgroup
-// per resident slot: 256 CUs, one 8-wave workgroup per CU at the score
-// kernel's register use (two 4-wave ones when a KV head has at most 256
-// window queries).  The length is a multiple of G (so no G-block straddles two
-// workgroups), at least the multiple of G nearest 1024 from below (or G) and
-// at most 8192 keys.
-int32_t chunk_keys_for(int32_t G, int32_t hq, int32_t hkv, int32_t n, int64_t max_tokens) {
-  const int32_t base = G >= 1024 ? G : G * (1024 / G);
-  if (hkv < 1 || hq < hkv || n < 1) return base;
-  const int64_t qn = (int64_t)(hq / hkv) * n;
-  const int64_t zsplit = qn <= 256 ? 1 : (qn + 511) / 512;
-  const int64_t slots = qn <= 256 ? 512 : 256;
-  const int64_t want = (max_tokens * hkv * zsplit + slots - 1) / slots;
-  const int64_t cap = base > 8192 ? base : 8192;
-  int64_t ck = (want + base - 1) / base * base;
-  if (ck < base) ck = base;
-  if (ck > cap) ck = cap / base * base;
-  return (int32_t)ck;
-}
 
 struct SelectLayout {
   size_t cu, blk, chunk, keep, scores, chunk_lse, lse, row_lse, total;
@@ -69,7 +48,7 @@ up_status plan_select(const up_select_params* prm, int32_t R, int64_t max_tokens
   if (R < 0 || max_tokens < 0 || max_tokens > INT32_MAX) return UP_ERR_SHAPE;
   const int32_t G = prm->block_size;
   L->scoring = (prm->flags & UP_SCORES_IN) == 0u;
-  L->chunk_keys = chunk_keys_for(G, prm->num_heads_q, prm->num_heads_kv, prm->window, max_tokens);
+  L->chunk_keys = up::chunk_keys_for(G, prm->num_heads_q, prm->num_heads_kv, prm->window, max_tokens);
   L->max_blocks = max_tokens / G + R;
   L->max_chunks = max_tokens / L->chunk_keys + R;
   const int64_t rows = (int64_t)prm->num_heads_q * prm->window;
@@ -304,6 +283,66 @@ up_status up_update_metadata(int32_t layer, int32_t num_layers, int32_t num_reqs
                           drop_len, max_drops, seqused_base, stream) != hipSuccess)
     return UP_ERR_HIP;
   return UP_OK;
+}
+
+up_status up_slot_mapping(const int32_t* block_table, int64_t block_table_stride,
+                          int32_t max_blocks_per_req, int32_t kv_block_size,
+                          const int32_t* cu_seqlens, const int32_t* seq_lens, int32_t num_reqs,
+                          int64_t max_tokens, int64_t* slot_mapping, hipStream_t stream) {
+  if (num_reqs < 0 || max_tokens < 0 || max_tokens > INT32_MAX) return UP_ERR_SHAPE;
+  if (max_blocks_per_req < 0 || block_table_stride < max_blocks_per_req) return UP_ERR_SHAPE;
+  if (kv_block_size < 1) return UP_ERR_PARAM;
+  if (cu_seqlens == nullptr || seq_lens == nullptr || slot_mapping == nullptr) return UP_ERR_NULL;
+  if (block_table == nullptr && max_blocks_per_req > 0) return UP_ERR_NULL;
+  if (!aligned(cu_seqlens, 4) || !aligned(seq_lens, 4) || !aligned(block_table, 4) ||
+      !aligned(slot_mapping, 8))
+    return UP_ERR_ALIGN;
+  up::SlotArgs a{};
+  a.table = block_table;
+  a.table_stride = block_table_stride;
+  a.width = max_blocks_per_req;
+  a.B = kv_block_size;
+  a.cu = cu_seqlens;
+  a.seq_lens = seq_lens;
+  a.R = num_reqs;
+  a.max_tokens = max_tokens;
+  a.slots = slot_mapping;
+  return up::launch_slots(a, stream) == hipSuccess ? UP_OK : UP_ERR_HIP;
+}
+
+up_status up_write_kv_cache(const void* key, int64_t key_row_stride, const void* value,
+                            int64_t value_row_stride, int64_t row_bytes, const int64_t* slot_mapping,
+                            const int32_t* cu_seqlens, int32_t num_reqs, int64_t max_tokens,
+                            void* key_cache, void* value_cache, int64_t cache_slots,
+                            hipStream_t stream) {
+  if (num_reqs < 0 || max_tokens < 0 || max_tokens > INT32_MAX || cache_slots < 0) return UP_ERR_SHAPE;
+  if (row_bytes < 4 || row_bytes % 4 != 0) return UP_ERR_PARAM;
+  if (key == nullptr || key_cache == nullptr || slot_mapping == nullptr || cu_seqlens == nullptr)
+    return UP_ERR_NULL;
+  if ((value == nullptr) != (value_cache == nullptr)) return UP_ERR_NULL;
+  if (key_row_stride < row_bytes || (value != nullptr && value_row_stride < row_bytes)) return UP_ERR_SHAPE;
+  if (key_row_stride % 4 != 0 || (value != nullptr && value_row_stride % 4 != 0)) return UP_ERR_ALIGN;
+  if (!aligned(key, 4) || !aligned(value, 4) || !aligned(key_cache, 4) || !aligned(value_cache, 4) ||
+      !aligned(slot_mapping, 8) || !aligned(cu_seqlens, 4))
+    return UP_ERR_ALIGN;
+  const bool vec = row_bytes % 16 == 0 && key_row_stride % 16 == 0 && aligned(key, 16) &&
+                   aligned(key_cache, 16) &&
+                   (value == nullptr || (value_row_stride % 16 == 0 && aligned(value, 16) &&
+                                         aligned(value_cache, 16)));
+  up::KvWriteArgs a{};
+  a.key = static_cast<const uint8_t*>(key);
+  a.key_stride = key_row_stride;
+  a.value = static_cast<const uint8_t*>(value);
+  a.value_stride = value == nullptr ? 0 : value_row_stride;
+  a.row_bytes = row_bytes;
+  a.slots = slot_mapping;
+  a.cu = cu_seqlens;
+  a.R = num_reqs;
+  a.max_tokens = max_tokens;
+  a.key_cache = static_cast<uint8_t*>(key_cache);
+  a.value_cache = static_cast<uint8_t*>(value_cache);
+  a.cache_slots = cache_slots;
+  return up::launch_kv_write(a, vec, stream) == hipSuccess ? UP_OK : UP_ERR_HIP;
 }
 
 }  // extern "C"

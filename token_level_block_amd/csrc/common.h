@@ -106,6 +106,37 @@ hipError_t launch_metadata(int32_t layer, int32_t L, int32_t R, const int32_t* c
                            int32_t max_drops, int32_t* seqused_base, hipStream_t s);
 
 // Tile sizes shared between the host planner and the kernels.
+// Eq. 16 slot mapping over the stream rows k < max_tokens
+struct SlotArgs {
+  const int32_t* table;      // [R][table_stride] physical block ids
+  int64_t table_stride;
+  int32_t width;             // usable columns per table row
+  int32_t B;                 // KV block size (tokens per physical block)
+  const int32_t* cu;         // [R+1] stream offsets of the requests
+  const int32_t* seq_lens;   // [R] patched lengths
+  int32_t R;
+  int64_t max_tokens;
+  int64_t* slots;            // out [max_tokens]
+};
+hipError_t launch_slots(const SlotArgs& a, hipStream_t s);
+
+// paged-cache write: cache row slots[k] <- key/value row k, k < min(cu[R], max_tokens)
+struct KvWriteArgs {
+  const uint8_t* key;
+  int64_t key_stride;        // bytes between consecutive key rows
+  const uint8_t* value;      // nullptr: keys only
+  int64_t value_stride;
+  int64_t row_bytes;         // bytes per cache row
+  const int64_t* slots;
+  const int32_t* cu;
+  int32_t R;
+  int64_t max_tokens;
+  uint8_t* key_cache;        // [cache_slots][row_bytes]
+  uint8_t* value_cache;
+  int64_t cache_slots;
+};
+hipError_t launch_kv_write(const KvWriteArgs& a, bool vec, hipStream_t s);
+
 constexpr int kCountTile = 4096;    // tokens per compaction count workgroup
 constexpr int kGatherTile = 256;    // tokens per compaction gather workgroup
 
