@@ -153,6 +153,54 @@ def measure_peaks(stream, ev):
     return mfma, copy
 
 
+def time_kv_cache(cu_out, seq_lens, R, kept, wl, stream, ev, reps, B=16):
+    """Eq. 16 slot mapping and the paged-cache write of the step's retained
+    rows (as the next layer would store them): random K and V rows of Hkv x d
+    bf16, KV block size 16, a shuffled block table; the MALL is flushed before
+    each timed call."""
+    import numpy as np
+    import torch
+    import token_level_block_amd as tlb
+    rb = wl.hkv * wl.d * 2
+    width = (kept + B - 1) // B + 1
+    rng = np.random.default_rng(wl.seed + 16)
+    table = torch.from_numpy(rng.permutation(R * width).astype(np.int32).reshape(R, width)).cuda()
+    key = torch.randint(-2 ** 15, 2 ** 15 - 1, (kept, rb // 2), dtype=torch.int16, device="cuda")
+    val = torch.randint(-2 ** 15, 2 ** 15 - 1, (kept, rb // 2), dtype=torch.int16, device="cuda")
+    kc = torch.empty((R * width * B, rb // 2), dtype=torch.int16, device="cuda")
+    vc = torch.empty_like(kc)
+    slots = torch.empty(kept, dtype=torch.int64, device="cuda")
+
+    def slot_call():
+        tlb.slot_mapping(table, width, width, B, cu_out, seq_lens, R, kept, slots, stream=stream)
+
+    def write_call():
+        tlb.write_kv_cache(key, rb, val, rb, rb, slots, cu_out, R, kept, kc, vc, R * width * B, stream=stream)
+
+    # reading 512 MB evicts the 256 MB MALL and leaves no dirty lines behind
+    # (a write-based flush would have them written back during the timed call)
+    flush = torch.ones(1 << 27, dtype=torch.int32, device="cuda")
+    sink = torch.empty((), dtype=torch.int64, device="cuda")
+
+    def mean_us(fn):
+        fn()
+        marks = [(ev.new(), ev.new()) for _ in range(reps)]
+        for a, b in marks:
+            torch.sum(flush, dim=0, dtype=torch.int64, out=sink)
+            ev.record(a, stream)
+            fn()
+            ev.record(b, stream)
+        return sum(ev.ms(a, b) for a, b in marks) / reps * 1e3
+
+    slot_us = mean_us(slot_call)
+    write_us = mean_us(write_call)
+    torch.cuda.synchronize()
+    nbytes = 2 * 2 * kept * rb + 8 * kept          # K and V rows read and written, slots read
+    return {"kernel": "kv_write_kernel", "bound": "hbm", "rows": kept, "row_bytes": rb, "kv_block_size": B,
+            "slot_mapping_us": slot_us, "write_us": write_us, "write_gbs": nbytes / (write_us * 1e-6) / 1e9,
+            "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+
+
 def threads_used():
     n = len(os.sched_getaffinity(0))
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
@@ -284,7 +332,15 @@ def main():
     sc_gbs = sc_bytes / ((select_ms + compact_ms) * 1e-3) / 1e9
     del qd, kd, hidden, out, full
     torch.cuda.empty_cache()
+    # the timed steps re-applied the same drop, so take the patched lengths of a
+    # single drop on a fresh prefill: the retained counts
+    retained = (cb.cu_out[1:R + 1] - cb.cu_out[:R]).to(torch.int32).contiguous()
+    kv = time_kv_cache(cb.cu_out, retained, R, kept, wl, stream, ev, args.steps)
+    log(f"[bench] Eq. 16 slot mapping {kv['slot_mapping_us']:.1f} us, KV-cache write {kv['write_us']:.1f} us "
+        f"({kv['write_gbs']:.0f} GB/s) for {kept} retained rows")
     mfma_peak, copy_peak = measure_peaks(stream, ev)
+    kv["frac"] = kv["write_gbs"] / PEAK_HBM_GBS
+    kv["frac_measured"] = kv["write_gbs"] / copy_peak
     log(f"[bench] measured peaks: bf16 MFMA {mfma_peak:.0f} TFLOP/s (random operands), copy {copy_peak:.0f} GB/s")
     ev.close()
 
@@ -327,6 +383,7 @@ def main():
         "hbm_select_compact": {"achieved": sc_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": sc_gbs / PEAK_HBM_GBS, "measured_peak": copy_peak,
                                "frac_measured": sc_gbs / copy_peak},
+        "kv_cache_eq16": kv,
         "measured_peaks": {"bf16_mfma_tflops": mfma_peak, "copy_gbs": copy_peak,
                            "how": "libuppeaks: random-operand 32x32x16 bf16 MFMA loop at 2 waves/SIMD; "
                                   "1 GiB streaming copy, read + write bytes"},

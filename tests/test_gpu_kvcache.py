@@ -90,7 +90,7 @@ def write_case(rng, rows, rb, nslots, strided, with_value):
 
 @pytest.mark.parametrize("rb,strided,with_value", [
     (4, False, True), (12, True, True), (16, False, True), (2048, False, True), (2048, True, True),
-    (4096, False, False), (2064, False, True)])
+    (4096, False, False), (2064, False, True), (1024, True, False), (8208, False, True), (8192, True, True)])
 def test_kv_write_matches_oracle(rb, strided, with_value):
     rng = np.random.default_rng(rb + strided)
     rows, nslots = 300, 512

@@ -10,7 +10,8 @@
 //           rows past cu[R].
 //   write : waves dealt round-robin over the rows; a wave copies its row's
 //           key (and value) to cache row `slot` with 16-byte accesses, the
-//           loads of both rows in flight before the stores.
+//           loads in flight before the stores (two rows per trip for rows of
+//           at most 4 KiB).
 #include "common.h"
 
 namespace up {
@@ -101,6 +102,58 @@ __global__ __launch_bounds__(kKvThreads) void kv_write_kernel(KvWriteArgs a) {
   }
 }
 
+// Rows of at most UPL KiB (UPL 16-byte units per lane): a wave moves two rows
+// per trip, so up to 4 * UPL loads per lane are in flight before the stores
+// (a 2 KiB K/V row pair alone would leave only two).
+template <int UPL>
+__global__ __launch_bounds__(kKvThreads) void kv_write_small_kernel(KvWriteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * kKvWaves + (threadIdx.x >> 6);
+  const int64_t W = (int64_t)gridDim.x * kKvWaves;
+  const int64_t T = a.R > 0 ? (int64_t)a.cu[a.R] : 0;
+  const int64_t count = T < 0 ? 0 : (T < a.max_tokens ? T : a.max_tokens);
+  const bool has_v = a.value != nullptr;
+  const int units = (int)(a.row_bytes >> 4);
+  for (int64_t k0 = gw; k0 < count; k0 += 2 * W) {
+    int64_t row[2] = {k0, k0 + W};
+    int64_t slot[2];
+    bool ok[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      slot[j] = row[j] < count ? a.slots[row[j]] : -1;
+      ok[j] = slot[j] >= 0 && slot[j] < a.cache_slots;
+    }
+    u32x4 kv[2][UPL], vv[2][UPL];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const u32x4* ks = reinterpret_cast<const u32x4*>(a.key + row[j] * a.key_stride);
+#pragma unroll
+      for (int x = 0; x < UPL; ++x)
+        if (ok[j] && lane + x * kWave < units) kv[j][x] = __builtin_nontemporal_load(ks + lane + x * kWave);
+      if (has_v) {
+        const u32x4* vs = reinterpret_cast<const u32x4*>(a.value + row[j] * a.value_stride);
+#pragma unroll
+        for (int x = 0; x < UPL; ++x)
+          if (ok[j] && lane + x * kWave < units) vv[j][x] = __builtin_nontemporal_load(vs + lane + x * kWave);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (!ok[j]) continue;
+      u32x4* kd = reinterpret_cast<u32x4*>(a.key_cache + slot[j] * a.row_bytes);
+#pragma unroll
+      for (int x = 0; x < UPL; ++x)
+        if (lane + x * kWave < units) kd[lane + x * kWave] = kv[j][x];
+      if (has_v) {
+        u32x4* vd = reinterpret_cast<u32x4*>(a.value_cache + slot[j] * a.row_bytes);
+#pragma unroll
+        for (int x = 0; x < UPL; ++x)
+          if (lane + x * kWave < units) vd[lane + x * kWave] = vv[j][x];
+      }
+    }
+  }
+}
+
 hipError_t launch_slots(const SlotArgs& a, hipStream_t s) {
   if (a.max_tokens <= 0) return hipSuccess;
   const unsigned grid = (unsigned)((a.max_tokens + kSlotThreads - 1) / kSlotThreads);
@@ -113,7 +166,13 @@ hipError_t launch_kv_write(const KvWriteArgs& a, bool vec, hipStream_t s) {
   // enough waves to fill the chip (256 CUs x 32 waves), fewer for small batches
   int64_t want = (a.max_tokens + kKvWaves - 1) / kKvWaves;
   want = want < 1 ? 1 : (want > 2048 ? 2048 : want);
-  if (vec)
+  if (vec && a.row_bytes <= 1024)
+    hipLaunchKernelGGL(kv_write_small_kernel<1>, dim3((unsigned)want), dim3(kKvThreads), 0, s, a);
+  else if (vec && a.row_bytes <= 2048)
+    hipLaunchKernelGGL(kv_write_small_kernel<2>, dim3((unsigned)want), dim3(kKvThreads), 0, s, a);
+  else if (vec && a.row_bytes <= 4096)
+    hipLaunchKernelGGL(kv_write_small_kernel<4>, dim3((unsigned)want), dim3(kKvThreads), 0, s, a);
+  else if (vec)
     hipLaunchKernelGGL(kv_write_kernel<true>, dim3((unsigned)want), dim3(kKvThreads), 0, s, a);
   else
     hipLaunchKernelGGL(kv_write_kernel<false>, dim3((unsigned)want), dim3(kKvThreads), 0, s, a);
