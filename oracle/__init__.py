@@ -28,4 +28,6 @@ from .uniprefill_oracle import (  # noqa: F401
     retained_positions,
     slot_mapping,
     write_kv_cache,
+    silu,
+    ffn_swiglu,
 )

@@ -327,3 +327,28 @@ def write_kv_cache(key_cache, value_cache, slots, key, value, count: int):
             if vc is not None:
                 vc[s] = value[i]
     return kc, vc
+
+
+# ---------------------------------------------------------------------------
+# A downstream sublayer on the retained set: UniPrefill Sec. 3.4 Eq. 7 (each
+# sublayer after a drop maps only the retained rows) and Eq. 9-10 (the saved
+# cost is the dropped share of every later sublayer's O(N d^2))
+# ---------------------------------------------------------------------------
+def silu(z):
+    """z * sigmoid(z)."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def ffn_swiglu(x_bits, w_gate_up_bits, w_down_bits):
+    """Gated FFN of the LLaMA family (SwiGLU), token by token:
+        g = x Wg^T, u = x Wu^T, h = silu(g) * u, y = h Wd^T
+    x [rows, D], w_gate_up [2F, D] (gate rows first, then up rows),
+    w_down [D, F], all bf16 bit patterns; float64 throughout."""
+    x = bf16_bits_to_f64(np.asarray(x_bits))
+    w = bf16_bits_to_f64(np.asarray(w_gate_up_bits))
+    wd = bf16_bits_to_f64(np.asarray(w_down_bits))
+    F = w.shape[0] // 2
+    g = x @ w[:F].T
+    u = x @ w[F:].T
+    return (silu(g) * u) @ wd.T

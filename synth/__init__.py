@@ -254,6 +254,73 @@ def hidden_words_torch_at(rows, nwords: int):
 
 
 # ---------------------------------------------------------------------------
+# Dense bf16 tensors for the downstream FFN sublayer: element (i, j) of tensor
+# `tag` (row-major, ncols columns) is a fixed function of (tag, i*ncols + j):
+# the murmur3 32-bit finalizer of the counter (mod 2^32) plus tag * 0x9E3779B1,
+# whose top 24 bits k give the value (k - 2^23) / 2^23 * 2^scale_log2 (uniform
+# on [-2^s, 2^s), exact in float32), rounded to bf16 (round to nearest even).
+# Any row range can be generated on its own, on the host or on a device, with
+# the same bits.
+# ---------------------------------------------------------------------------
+FFN_INTERMEDIATE = {"llama8b": 14336, "gemma3": 15360}
+_TAGMUL = 0x9E3779B1
+_FM1, _FM2 = 0x85EBCA6B, 0xC2B2AE35
+_M32 = 0xFFFFFFFF
+
+
+def uniform_bf16_bits(tag: int, row0: int, nrows: int, ncols: int, scale_log2: int) -> np.ndarray:
+    """uint16 [nrows, ncols]: rows row0 .. row0+nrows-1 of tensor `tag`, on
+    the host (computed with torch on the CPU, the same code as on a device)."""
+    import torch
+    t = uniform_bf16_torch(tag, row0, nrows, ncols, scale_log2, "cpu")
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def uniform_bf16_torch(tag: int, row0: int, nrows: int, ncols: int, scale_log2: int, device,
+                       chunk_rows: int = 4096):
+    """Same values as uniform_bf16_bits, as a torch bfloat16 tensor on `device`."""
+    import torch
+    out = torch.empty((nrows, ncols), dtype=torch.bfloat16, device=device)
+    col = torch.arange(ncols, dtype=torch.int64, device=device)[None, :]
+    base = (tag * _TAGMUL) & _M32
+    for a in range(0, nrows, chunk_rows):
+        z = min(nrows, a + chunk_rows)
+        rows = torch.arange(row0 + a, row0 + z, dtype=torch.int64, device=device)[:, None]
+        h = (rows * ncols + col + base) & _M32
+        h ^= h >> 16
+        h = (h * _FM1) & _M32
+        h ^= h >> 13
+        h = (h * _FM2) & _M32
+        h ^= h >> 16
+        k = (h >> 8) - (1 << 23)
+        out[a:z] = (k.to(torch.float32) * (2.0 ** (scale_log2 - 23))).to(torch.bfloat16)
+    return out
+
+
+def ffn_weights(D: int, F: int, seed: int = 7):
+    """(w_gate_up [2F, D], w_down [D, F]) bf16 bits; entries uniform with
+    scale 2^-6, so a unit-range activation row gives gate and up values of
+    order 0.3 and outputs of order 0.1."""
+    return (uniform_bf16_bits(2 * seed + 1, 0, 2 * F, D, -6),
+            uniform_bf16_bits(2 * seed + 2, 0, D, F, -6))
+
+
+def ffn_weights_torch(D: int, F: int, device, seed: int = 7):
+    """ffn_weights as bfloat16 tensors on `device`."""
+    return (uniform_bf16_torch(2 * seed + 1, 0, 2 * F, D, -6, device),
+            uniform_bf16_torch(2 * seed + 2, 0, D, F, -6, device))
+
+
+def ffn_activations(rows: int, D: int, seed: int = 7, row0: int = 0):
+    """bf16 bits [rows, D], entries uniform on [-1, 1)."""
+    return uniform_bf16_bits(2 * seed + 3, row0, rows, D, 0)
+
+
+def ffn_activations_torch(rows: int, D: int, device, seed: int = 7, row0: int = 0):
+    return uniform_bf16_torch(2 * seed + 3, row0, rows, D, 0, device)
+
+
+# ---------------------------------------------------------------------------
 # The five workloads.
 # ---------------------------------------------------------------------------
 def llama_4k(seed: int = 0) -> Workload:

@@ -474,4 +474,81 @@ def check_kv_write(impl):
 SLOT_CHECKS = [check_slot_fixture, check_slot_closed_form, check_slot_structure,
                check_slot_eq17_consistency, check_kv_write]
 
-ALL_CHECKS = SCORE_CHECKS + TOPP_CHECKS + COMPACT_CHECKS + SLOT_CHECKS
+# ---------------------------------------------------------------------------
+# A downstream sublayer on the retained set (Eq. 7): the gated FFN
+# ---------------------------------------------------------------------------
+def check_ffn_fixture(impl):
+    g = load_golden("ffn_swiglu_example.json")
+    y = impl.ffn_swiglu(bf16_bits(np.array([g["x"]])), bf16_bits(np.array(g["w_gate_up"])),
+                        bf16_bits(np.array(g["w_down"])))
+    assert np.allclose(y[0], g["y"], rtol=1e-15, atol=0), y
+
+
+def check_silu(impl):
+    """SiLU against torch's own (CPU, float64) and its odd part: silu(z) -
+    silu(-z) = z."""
+    import torch
+    rng = np.random.default_rng(31)
+    z = np.concatenate([np.linspace(-40.0, 40.0, 2001), 6.0 * rng.standard_normal(2000)])
+    ref = torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    s = impl.silu(z)
+    assert np.allclose(s, ref, rtol=1e-14, atol=1e-300)
+    assert np.allclose(s - impl.silu(-z), z, rtol=1e-12, atol=1e-12)
+    assert impl.silu(np.array([0.0]))[0] == 0.0
+
+
+def _ffn_case(rng, rows, D, F):
+    x = bf16_bits(rng.uniform(-1, 1, size=(rows, D)))
+    w = bf16_bits(rng.uniform(-0.1, 0.1, size=(2 * F, D)))
+    wd = bf16_bits(rng.uniform(-0.1, 0.1, size=(D, F)))
+    return x, w, wd
+
+
+def check_ffn_saturated_gates(impl):
+    """A gate fixed at +30 makes the FFN the plain product 30 (x Wu^T) Wd^T
+    (silu(30) = 30 within 1e-11); a gate of -30 silences it."""
+    rng = np.random.default_rng(32)
+    rows, D, F = 7, 12, 9
+    x, w, wd = _ffn_case(rng, rows, D, F)
+    x[:, 0] = bf16_bits(np.ones(rows))          # a constant input column drives the gates
+    for gate, want_scale in ((30.0, 30.0), (-30.0, 0.0)):
+        wg = np.zeros((F, D))
+        wg[:, 0] = gate
+        ww = w.copy()
+        ww[:F] = bf16_bits(wg)
+        y = impl.ffn_swiglu(x, ww, wd)
+        u = bits_to_f64(x) @ bits_to_f64(w[F:]).T
+        ref = want_scale * (u @ bits_to_f64(wd).T)
+        assert np.allclose(y, ref, rtol=1e-10, atol=1e-9 * max(1.0, np.abs(ref).max())), gate
+
+
+def check_ffn_linearity(impl):
+    """Linear in the up and down weights (doubling either doubles y exactly);
+    not linear in the gate."""
+    rng = np.random.default_rng(33)
+    rows, D, F = 5, 16, 11
+    x, w, wd = _ffn_case(rng, rows, D, F)
+    y = impl.ffn_swiglu(x, w, wd)
+    w2 = w.copy()
+    w2[F:] = bf16_bits(2.0 * bits_to_f64(w[F:]))
+    assert np.allclose(impl.ffn_swiglu(x, w2, wd), 2.0 * y, rtol=1e-14, atol=0)
+    assert np.allclose(impl.ffn_swiglu(x, w, bf16_bits(2.0 * bits_to_f64(wd))), 2.0 * y, rtol=1e-14, atol=0)
+    wg2 = w.copy()
+    wg2[:F] = bf16_bits(2.0 * bits_to_f64(w[:F]))
+    assert not np.allclose(impl.ffn_swiglu(x, wg2, wd), 2.0 * y, rtol=1e-3)
+
+
+def check_ffn_rows_independent(impl):
+    """Token-wise: the FFN of the retained rows is the retained rows of the FFN
+    of the full stream (what lets later sublayers run on the compacted
+    stream, Eq. 7)."""
+    rng = np.random.default_rng(34)
+    x, w, wd = _ffn_case(rng, 40, 16, 24)
+    keep = rng.random(40) < 0.4
+    assert np.allclose(impl.ffn_swiglu(x[keep], w, wd), impl.ffn_swiglu(x, w, wd)[keep], rtol=1e-13, atol=1e-15)
+
+
+FFN_CHECKS = [check_ffn_fixture, check_silu, check_ffn_saturated_gates, check_ffn_linearity,
+              check_ffn_rows_independent]
+
+ALL_CHECKS = SCORE_CHECKS + TOPP_CHECKS + COMPACT_CHECKS + SLOT_CHECKS + FFN_CHECKS

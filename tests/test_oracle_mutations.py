@@ -199,6 +199,25 @@ def _kv_write_all_rows(key_cache, value_cache, slots, key, value, count):
     return U.write_kv_cache(key_cache, value_cache, slots, key, value, len(slots))
 
 
+def _ffn_variant(act="silu", swap=False, no_up=False):
+    def ffn_swiglu(x_bits, w_gate_up_bits, w_down_bits):
+        x = U.bf16_bits_to_f64(np.asarray(x_bits))
+        w = U.bf16_bits_to_f64(np.asarray(w_gate_up_bits))
+        wd = U.bf16_bits_to_f64(np.asarray(w_down_bits))
+        F = w.shape[0] // 2
+        g, u = x @ w[:F].T, x @ w[F:].T
+        if swap:
+            g, u = u, g
+        a = {"silu": U.silu, "relu": lambda z: np.maximum(z, 0.0), "sigmoid": lambda z: 1.0 / (1.0 + np.exp(-z))}[act](g)
+        h = a if no_up else a * u
+        return h @ wd.T
+    return ffn_swiglu
+
+
+def _silu_sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64)))
+
+
 MUTANTS = {
     "head_mean": _scoring_mutant(ti_kw=dict(head_mean=True)),
     "no_causal_mask": _scoring_mutant(ti_kw=dict(causal=False)),
@@ -224,6 +243,11 @@ MUTANTS = {
     "slot_context_off_by_one": _slot_variant(positions="context_plus_one"),
     "slot_div_mod_swapped": _slot_variant(swap_div_mod=True),
     "kv_write_ignores_count": _namespace(write_kv_cache=_kv_write_all_rows),
+    "ffn_gate_up_swapped": _namespace(ffn_swiglu=_ffn_variant(swap=True)),
+    "ffn_relu_gate": _namespace(ffn_swiglu=_ffn_variant(act="relu")),
+    "ffn_sigmoid_gate": _namespace(ffn_swiglu=_ffn_variant(act="sigmoid")),
+    "ffn_no_up_projection": _namespace(ffn_swiglu=_ffn_variant(no_up=True)),
+    "silu_is_sigmoid": _namespace(silu=_silu_sigmoid),
 }
 
 
