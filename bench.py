@@ -201,6 +201,46 @@ def time_kv_cache(cu_out, seq_lens, R, kept, wl, stream, ev, reps, B=16):
             "peak": PEAK_HBM_GBS, "unit": "GB/s"}
 
 
+def time_ffn(keep_mask, cu_d, R, T, kept, wl, stream, ev, reps=3):
+    """Eq. 7 / Eq. 10 in practice: the layer's gated FFN (LLaMA-3.1-8B widths,
+    seeded synthetic weights and activations) on the retained rows against
+    the same FFN on the full stream."""
+    import torch
+    import synth
+    import token_level_block_amd as tlb
+    from token_level_block_amd.runner import CompactBuffers
+    D = wl.hidden
+    F = synth.FFN_INTERMEDIATE["llama8b"]
+    wg, wd = synth.ffn_weights_torch(D, F, "cuda")
+    x = synth.ffn_activations_torch(T, D, "cuda")
+    xc = torch.empty_like(x)
+    cb = CompactBuffers.allocate(R, T)
+    cb.run(keep_mask, cu_d, [x.view(torch.int16)], [xc.view(torch.int16)], stream=stream)
+    ffn = tlb.FFN(D, F)
+    ws = torch.empty(ffn.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+
+    def mean_ms(inp, rows):
+        ffn.forward(inp, rows, wg, wd, y, ws, stream=stream)
+        marks = [(ev.new(), ev.new()) for _ in range(reps)]
+        for a, b in marks:
+            ev.record(a, stream)
+            ffn.forward(inp, rows, wg, wd, y, ws, stream=stream)
+            ev.record(b, stream)
+        return sum(ev.ms(a, b) for a, b in marks) / reps
+
+    ms_full = mean_ms(x, T)
+    ms_kept = mean_ms(xc, kept)
+    torch.cuda.synchronize()
+    ffn.close()
+    flops = lambda rows: 6.0 * rows * D * F
+    return {"hidden": D, "intermediate": F, "rows_full": T, "rows_kept": kept,
+            "ms_full": ms_full, "ms_kept": ms_kept,
+            "tflops_full": flops(T) / (ms_full * 1e-3) / 1e12, "tflops_kept": flops(kept) / (ms_kept * 1e-3) / 1e12,
+            "saving_measured": 1.0 - ms_kept / ms_full, "saving_eq10": 1.0 - kept / T,
+            "gemms": "hipBLASLt bf16, fp32 accumulate; SwiGLU in swiglu_kernel"}
+
+
 def threads_used():
     n = len(os.sched_getaffinity(0))
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
@@ -338,6 +378,9 @@ def main():
     kv = time_kv_cache(cb.cu_out, retained, R, kept, wl, stream, ev, args.steps)
     log(f"[bench] Eq. 16 slot mapping {kv['slot_mapping_us']:.1f} us, KV-cache write {kv['write_us']:.1f} us "
         f"({kv['write_gbs']:.0f} GB/s) for {kept} retained rows")
+    ffn = time_ffn(sel.keep_mask, cu_d, R, T, kept, wl, stream, ev)
+    log(f"[bench] FFN on {kept} retained rows {ffn['ms_kept']:.2f} ms vs {T} rows {ffn['ms_full']:.2f} ms: "
+        f"saving {ffn['saving_measured']:.3f} (Eq. 10: {ffn['saving_eq10']:.3f})")
     mfma_peak, copy_peak = measure_peaks(stream, ev)
     kv["frac"] = kv["write_gbs"] / PEAK_HBM_GBS
     kv["frac_measured"] = kv["write_gbs"] / copy_peak
@@ -384,6 +427,7 @@ def main():
                                "frac": sc_gbs / PEAK_HBM_GBS, "measured_peak": copy_peak,
                                "frac_measured": sc_gbs / copy_peak},
         "kv_cache_eq16": kv,
+        "ffn_eq7": ffn,
         "measured_peaks": {"bf16_mfma_tflops": mfma_peak, "copy_gbs": copy_peak,
                            "how": "libuppeaks: random-operand 32x32x16 bf16 MFMA loop at 2 waves/SIMD; "
                                   "1 GiB streaming copy, read + write bytes"},

@@ -247,6 +247,42 @@ up_status up_write_kv_cache(const void* key, int64_t key_row_stride, const void*
                             void* key_cache, void* value_cache, int64_t cache_slots,
                             hipStream_t stream);
 
+/*
+ * Downstream sublayer on the retained rows: the gated FFN of the LLaMA family,
+ * y = (silu(x Wg^T) * (x Wu^T)) Wd^T row by row.  UniPrefill Sec. 3.4 Eq. 7:
+ * after a drop every later sublayer (FFN included) maps only the retained
+ * rows, which is the saving Eq. 9-10 counts; calling it on the compacted
+ * stream instead of the full one is that saving.
+ *
+ * up_ffn_create   host-side set-up for hidden width D and intermediate width F
+ *                 (both positive multiples of 8): a hipBLASLt handle and GEMM
+ *                 descriptors.  Unlike every other call it allocates (host
+ *                 objects, and whatever hipBLASLt allocates for its handle);
+ *                 create once, reuse.  UP_ERR_PARAM on bad widths, UP_ERR_HIP
+ *                 if hipBLASLt fails.
+ * up_ffn_destroy  releases it (NULL is a no-op).
+ * up_ffn_workspace_bytes  device workspace up_ffn_forward needs for `rows`:
+ *                 rows x 2F bf16 (gate/up product) + rows x F bf16 (activation)
+ *                 + 64 MiB of GEMM scratch.
+ * up_ffn_forward  x bf16 [rows][D]; w_gate_up bf16 [2F][D] (gate rows, then up
+ *                 rows: the [out][in] layout of a linear layer); w_down bf16
+ *                 [D][F]; y bf16 out [rows][D].  GEMMs accumulate in fp32; the
+ *                 gate/up product and the activation are rounded to bf16.
+ *                 rows is a host value (e.g. the kept count read back once
+ *                 the compaction has run); rows == 0 does nothing.  All
+ *                 pointers 16-byte aligned.  One up_ffn must not be used by two
+ *                 threads at once (it caches the GEMM choice for the last row
+ *                 count).  Errors: UP_ERR_NULL, UP_ERR_SHAPE, UP_ERR_ALIGN,
+ *                 UP_ERR_WORKSPACE, UP_ERR_HIP.
+ */
+typedef struct up_ffn up_ffn;
+up_status up_ffn_create(int32_t hidden, int32_t intermediate, up_ffn** out);
+void up_ffn_destroy(up_ffn* ffn);
+size_t up_ffn_workspace_bytes(const up_ffn* ffn, int64_t rows);
+up_status up_ffn_forward(up_ffn* ffn, const void* x, int64_t rows, const void* w_gate_up,
+                         const void* w_down, void* y, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 /* Static description of a status code. */
 const char* up_status_string(up_status status);
 

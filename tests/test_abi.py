@@ -237,3 +237,14 @@ def test_slot_mapping_and_kv_write_reject():
     assert kv(ks=2050) == tlb.UP_ERR_ALIGN
     assert kv(k=FAKE + 2) == tlb.UP_ERR_ALIGN
     assert kv(sl=FAKE + 4) == tlb.UP_ERR_ALIGN
+
+
+def test_ffn_rejects_before_any_hip_work():
+    assert tlb.ffn_create_status(0, 64) == tlb.UP_ERR_PARAM
+    assert tlb.ffn_create_status(4096, 14330) == tlb.UP_ERR_PARAM     # not a multiple of 8
+    assert tlb.ffn_create_status(-8, 64) == tlb.UP_ERR_PARAM
+    lib = tlb._lib
+    assert lib.up_ffn_create(64, 64, None) == tlb.UP_ERR_NULL
+    assert lib.up_ffn_workspace_bytes(None, 10) == 0
+    assert lib.up_ffn_forward(None, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == tlb.UP_ERR_NULL
+    lib.up_ffn_destroy(None)

@@ -6,7 +6,8 @@
 is being rebuilt).
 
 Every .hip file under csrc/ is compiled to an object in _build/ and linked
-into token_level_block_amd/libuniprefill.so.  peaks/peaks.hip (reference
+into token_level_block_amd/libuniprefill.so (with hipBLASLt, which the FFN
+sublayer's two projections use).  peaks/peaks.hip (reference
 MFMA and copy rates, loaded only by the benchmark) becomes libuppeaks.so.
 Packed fp32 instructions are disabled for all device code.
 """
@@ -72,16 +73,16 @@ def build(verbose: bool = True) -> str:
         if warn.strip() and verbose:
             print(warn, file=sys.stderr)
     objs = [o for o, _ in results]
-    _link(hipcc, objs[:-1], LIB)
+    _link(hipcc, objs[:-1], LIB, ["-L/opt/rocm/lib", "-lhipblaslt"])
     _link(hipcc, objs[-1:], PEAKS_LIB)
     if verbose:
         print(f"built {LIB} and {PEAKS_LIB}")
     return LIB
 
 
-def _link(hipcc, objs, out):
+def _link(hipcc, objs, out, libs=()):
     tmp = out + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *libs]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{p.stdout}\n{p.stderr}")
