@@ -309,39 +309,84 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     ev = HipEvents()
 
-    def step(marks=None):
+    def step(s, marks=None):
         if marks is not None:
             prm.prof_score_begin, prm.prof_score_end = marks["score"]
-            ev.record(marks["t0"], stream)
+            ev.record(marks["t0"], s)
         else:
             prm.prof_score_begin = prm.prof_score_end = None
-        sel.run(qd, kd, cu_d, stream=stream)
+        sel.run(qd, kd, cu_d, stream=s)
         if marks is not None:
-            ev.record(marks["t1"], stream)
-        cb.run(sel.keep_mask, cu_d, [hidden], [out], stream=stream)
+            ev.record(marks["t1"], s)
+        cb.run(sel.keep_mask, cu_d, [hidden], [out], stream=s)
         if marks is not None:
-            ev.record(marks["t2"], stream)
-        mb.run(0, cu_d, cb.cu_out, stream=stream)
+            ev.record(marks["t2"], s)
+        mb.run(0, cu_d, cb.cu_out, stream=s)
         if marks is not None:
-            ev.record(marks["t3"], stream)
-        run_scatter_back(out, cb.index_out, cb.cu_out, R, T, full, stream=stream)
+            ev.record(marks["t3"], s)
+        run_scatter_back(out, cb.index_out, cb.cu_out, R, T, full, stream=s)
         if marks is not None:
-            ev.record(marks["t4"], stream)
+            ev.record(marks["t4"], s)
+
+    def timed(run_one):
+        start, stop = ev.new(), ev.new()
+        torch.cuda.synchronize()
+        ev.record(start, stream)
+        for _ in range(args.steps):
+            run_one()
+        ev.record(stop, stream)
+        torch.cuda.synchronize()
+        return ev.ms(start, stop) / args.steps
 
     for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+        step(stream)
+    # K plain steps (launched one call at a time) ...
+    ms_eager = timed(lambda: step(stream))
+    # the live part of every output (entries past the kept rows are never written)
+    kept_now = int(cb.cu_out[R].item())
+
+    def live():
+        return (sel.keep_mask[:T], sel.kept[:R], cb.cu_out, cb.index_out[:kept_now], out[:kept_now], full)
+    ref_out = [t.clone() for t in live()]
+    # ... K more with events between the phases, for the per-kernel breakdown
     marks = [dict(score=(ev.new(), ev.new()), t0=ev.new(), t1=ev.new(), t2=ev.new(), t3=ev.new(), t4=ev.new())
              for _ in range(args.steps)]
-    start, stop = ev.new(), ev.new()
     torch.cuda.synchronize()
-    ev.record(start, stream)
     for i in range(args.steps):
-        step(marks[i])
-    ev.record(stop, stream)
+        step(stream, marks[i])
     torch.cuda.synchronize()
-    total_ms = ev.ms(start, stop)
-    ms_per_step = total_ms / args.steps
+
+    # ... and the same step captured once in a HIP graph and replayed K times
+    # (every call only enqueues kernels, so the whole step is capturable); each
+    # of three checked replays must reproduce the eager step's outputs bit for bit
+    ms_graph, graph_note = None, None
+    try:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(side.cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            for t in (sel.keep_mask, out):
+                t.zero_()
+            step(stream)                 # eager work between replays
+            for t in (sel.keep_mask, out):
+                t.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(a, b) for a, b in zip(live(), ref_out)):
+                raise RuntimeError("a graph replay differs from the eager step")
+        ms_graph = timed(graph.replay)
+    except Exception as e:       # report the eager figure only
+        graph_note = f"graph replay not used: {e}"
+        log(f"[bench] {graph_note}")
+    ms_per_step = ms_graph if ms_graph is not None else ms_eager
+
     def mean(a, b):
         return sum(ev.ms(m[a], m[b]) for m in marks) / len(marks)
 
@@ -363,6 +408,8 @@ def main():
     compact_gbs = compact_bytes / (compact_ms * 1e-3) / 1e9
     scatter_bytes = 2 * kept * row_bytes + 4 * kept
     scatter_gbs = scatter_bytes / (scatter_ms * 1e-3) / 1e9
+    log(f"[bench] eager {ms_eager:.3f} ms/step, graph replay "
+        f"{'-' if ms_graph is None else f'{ms_graph:.3f}'} ms/step")
     log(f"[bench] {ms_per_step:.3f} ms/step  select {select_ms:.3f} (score {score_ms:.3f}) compact "
         f"{compact_ms:.3f} metadata {meta_ms:.3f} scatter {scatter_ms:.3f}  kept {kept}/{T}")
     # select + compact as HBM work (the score GEMM's K reads are counted under MFMA):
@@ -431,6 +478,9 @@ def main():
         "measured_peaks": {"bf16_mfma_tflops": mfma_peak, "copy_gbs": copy_peak,
                            "how": "libuppeaks: random-operand 32x32x16 bf16 MFMA loop at 2 waves/SIMD; "
                                   "1 GiB streaming copy, read + write bytes"},
+        "launch": "hip_graph" if ms_graph is not None else f"eager ({graph_note})",
+        "ms_per_step_eager": ms_eager,
+        "ms_per_step_graph": ms_graph,
         "breakdown_ms": {"select": select_ms, "score_kernel": score_ms, "compact": compact_ms,
                          "metadata": meta_ms, "scatter_back": scatter_ms},
         "select_compact_tokens_per_s": sel_compact_tps,
