@@ -153,12 +153,21 @@ __global__ __launch_bounds__(kGatherThreads) void rank_kernel(CompactArgs a) {
 // ---------------------------------------------------------------------------
 // Row copy over the kept rows k < count:  kGather: dst row k <- src row map[k]
 //                                         scatter: dst row map[k] <- src row k
-// Rows are dealt round-robin to waves; a wave moves one row at a time with up
-// to eight 16-byte nontemporal loads in flight per lane (the rows are streamed
-// once, so they bypass cache residency).
+// 16-byte path: each wave takes a contiguous range of rows (an even number, the
+// same for every busy wave: ceil(count / waves) rounded up to even) and moves
+// two rows per trip, up to sixteen 16-byte nontemporal loads in flight per lane
+// (the rows are streamed once, so they bypass cache residency).  Equal ranges
+// keep the last trip from running on a fraction of the waves.  4-byte path:
+// rows dealt round-robin, one per trip.
 // ---------------------------------------------------------------------------
 constexpr int kCopyThreads = 256;
 constexpr int kCopyWaves = kCopyThreads / kWave;
+
+template <bool kGather>
+__device__ __forceinline__ void row_ends(const int32_t* __restrict__ map, int64_t k, int64_t& s, int64_t& d) {
+  s = kGather ? (int64_t)map[k] : k;
+  d = kGather ? k : (int64_t)map[k];
+}
 
 template <bool kGather, bool kVec>
 __global__ __launch_bounds__(kCopyThreads) void copy_rows_kernel(const uint8_t* __restrict__ src,
@@ -170,24 +179,46 @@ __global__ __launch_bounds__(kCopyThreads) void copy_rows_kernel(const uint8_t* 
   const int64_t gw = (int64_t)blockIdx.x * kCopyWaves + (threadIdx.x >> 6);
   const int64_t W = (int64_t)gridDim.x * kCopyWaves;
   const int64_t count = min<int64_t>(*count_ptr, max_rows);
-  for (int64_t k = gw; k < count; k += W) {
-    const int64_t s = kGather ? (int64_t)map[k] : k;
-    const int64_t d = kGather ? k : (int64_t)map[k];
-    if (d < 0 || d >= dst_rows) continue;
-    if (kVec) {
-      const u32x4* sp = reinterpret_cast<const u32x4*>(src + s * rb);
-      u32x4* dp = reinterpret_cast<u32x4*>(dst + d * rb);
-      const int units = (int)(rb >> 4);
-      int u = lane;
-      for (; u + 7 * kWave < units; u += 8 * kWave) {
-        u32x4 v[8];
+  if (kVec) {
+    const int64_t per = (((count + W - 1) / W) + 1) & ~(int64_t)1;
+    const int64_t k0 = gw * per, k1 = min<int64_t>(count, k0 + per);
+    const int units = (int)(rb >> 4);
+    for (int64_t k = k0; k < k1; k += 2) {
+      int64_t s[2], d[2];
+      bool ok[2];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) v[x] = __builtin_nontemporal_load(sp + u + x * kWave);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) __builtin_nontemporal_store(v[x], dp + u + x * kWave);
+      for (int j = 0; j < 2; ++j) {
+        ok[j] = k + j < k1;
+        if (ok[j]) row_ends<kGather>(map, k + j, s[j], d[j]);
+        ok[j] = ok[j] && d[j] >= 0 && d[j] < dst_rows;
       }
-      for (; u < units; u += kWave) __builtin_nontemporal_store(__builtin_nontemporal_load(sp + u), dp + u);
-    } else {
+      for (int u0 = 0; u0 < units; u0 += 8 * kWave) {
+        u32x4 v[2][8];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const u32x4* sp = reinterpret_cast<const u32x4*>(src + (ok[j] ? s[j] : 0) * rb);
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int u = u0 + lane + x * kWave;
+            if (ok[j] && u < units) v[j][x] = __builtin_nontemporal_load(sp + u);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          u32x4* dp = reinterpret_cast<u32x4*>(dst + (ok[j] ? d[j] : 0) * rb);
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int u = u0 + lane + x * kWave;
+            if (ok[j] && u < units) __builtin_nontemporal_store(v[j][x], dp + u);
+          }
+        }
+      }
+    }
+  } else {
+    for (int64_t k = gw; k < count; k += W) {
+      int64_t s, d;
+      row_ends<kGather>(map, k, s, d);
+      if (d < 0 || d >= dst_rows) continue;
       const uint32_t* sp = reinterpret_cast<const uint32_t*>(src + s * rb);
       uint32_t* dp = reinterpret_cast<uint32_t*>(dst + d * rb);
       const int units = (int)(rb >> 2);
@@ -197,9 +228,9 @@ __global__ __launch_bounds__(kCopyThreads) void copy_rows_kernel(const uint8_t* 
 }
 
 static unsigned copy_grid(int64_t max_rows) {
-  // enough waves to fill the chip (256 CUs x 32 waves), fewer for small batches
+  // up to 256 CUs x 64 waves, fewer for small batches
   const int64_t want = (max_rows + kCopyWaves - 1) / kCopyWaves;
-  return (unsigned)(want < 1 ? 1 : (want > 2048 ? 2048 : want));
+  return (unsigned)(want < 1 ? 1 : (want > 4096 ? 4096 : want));
 }
 
 static hipError_t launch_copy(bool gather, bool vec, const uint8_t* src, uint8_t* dst, int64_t rb,
