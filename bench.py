@@ -241,6 +241,10 @@ def time_ffn(keep_mask, cu_d, R, T, kept, wl, stream, ev, reps=3):
             "gemms": "hipBLASLt bf16, fp32 accumulate; SwiGLU in swiglu_kernel"}
 
 
+def ratio(a, b):
+    return None if b is None else a / b
+
+
 def threads_used():
     n = len(os.sched_getaffinity(0))
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
@@ -256,6 +260,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step only: skip the next-row extras (Eq. 16 slots and KV write, the FFN) "
+                         "and the measured peaks (for short profiled runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -419,19 +426,22 @@ def main():
     sc_gbs = sc_bytes / ((select_ms + compact_ms) * 1e-3) / 1e9
     del qd, kd, hidden, out, full
     torch.cuda.empty_cache()
-    # the timed steps re-applied the same drop, so take the patched lengths of a
-    # single drop on a fresh prefill: the retained counts
-    retained = (cb.cu_out[1:R + 1] - cb.cu_out[:R]).to(torch.int32).contiguous()
-    kv = time_kv_cache(cb.cu_out, retained, R, kept, wl, stream, ev, args.steps)
-    log(f"[bench] Eq. 16 slot mapping {kv['slot_mapping_us']:.1f} us, KV-cache write {kv['write_us']:.1f} us "
-        f"({kv['write_gbs']:.0f} GB/s) for {kept} retained rows")
-    ffn = time_ffn(sel.keep_mask, cu_d, R, T, kept, wl, stream, ev)
-    log(f"[bench] FFN on {kept} retained rows {ffn['ms_kept']:.2f} ms vs {T} rows {ffn['ms_full']:.2f} ms: "
-        f"saving {ffn['saving_measured']:.3f} (Eq. 10: {ffn['saving_eq10']:.3f})")
-    mfma_peak, copy_peak = measure_peaks(stream, ev)
-    kv["frac"] = kv["write_gbs"] / PEAK_HBM_GBS
-    kv["frac_measured"] = kv["write_gbs"] / copy_peak
-    log(f"[bench] measured peaks: bf16 MFMA {mfma_peak:.0f} TFLOP/s (random operands), copy {copy_peak:.0f} GB/s")
+    kv = ffn = None
+    mfma_peak = copy_peak = None
+    if not args.step_only:
+        # the timed steps re-applied the same drop, so take the patched lengths of a
+        # single drop on a fresh prefill: the retained counts
+        retained = (cb.cu_out[1:R + 1] - cb.cu_out[:R]).to(torch.int32).contiguous()
+        kv = time_kv_cache(cb.cu_out, retained, R, kept, wl, stream, ev, args.steps)
+        log(f"[bench] Eq. 16 slot mapping {kv['slot_mapping_us']:.1f} us, KV-cache write {kv['write_us']:.1f} us "
+            f"({kv['write_gbs']:.0f} GB/s) for {kept} retained rows")
+        ffn = time_ffn(sel.keep_mask, cu_d, R, T, kept, wl, stream, ev)
+        log(f"[bench] FFN on {kept} retained rows {ffn['ms_kept']:.2f} ms vs {T} rows {ffn['ms_full']:.2f} ms: "
+            f"saving {ffn['saving_measured']:.3f} (Eq. 10: {ffn['saving_eq10']:.3f})")
+        mfma_peak, copy_peak = measure_peaks(stream, ev)
+        kv["frac"] = kv["write_gbs"] / PEAK_HBM_GBS
+        kv["frac_measured"] = kv["write_gbs"] / copy_peak
+        log(f"[bench] measured peaks: bf16 MFMA {mfma_peak:.0f} TFLOP/s (random operands), copy {copy_peak:.0f} GB/s")
     ev.close()
 
     cpu = None
@@ -463,16 +473,16 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "score_kernel<128>", "achieved": score_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": score_tflops / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),
-                     "measured_peak": mfma_peak, "frac_measured": score_tflops / mfma_peak},
+                     "measured_peak": mfma_peak, "frac_measured": ratio(score_tflops, mfma_peak)},
         "roofline_compact": {"bound": "hbm", "kernel": "up_compact", "achieved": compact_gbs,
                              "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": compact_gbs / PEAK_HBM_GBS,
-                             "measured_peak": copy_peak, "frac_measured": compact_gbs / copy_peak},
+                             "measured_peak": copy_peak, "frac_measured": ratio(compact_gbs, copy_peak)},
         "roofline_scatter": {"bound": "hbm", "kernel": "up_scatter_back", "achieved": scatter_gbs,
                              "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": scatter_gbs / PEAK_HBM_GBS,
-                             "measured_peak": copy_peak, "frac_measured": scatter_gbs / copy_peak},
+                             "measured_peak": copy_peak, "frac_measured": ratio(scatter_gbs, copy_peak)},
         "hbm_select_compact": {"achieved": sc_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": sc_gbs / PEAK_HBM_GBS, "measured_peak": copy_peak,
-                               "frac_measured": sc_gbs / copy_peak},
+                               "frac_measured": ratio(sc_gbs, copy_peak)},
         "kv_cache_eq16": kv,
         "ffn_eq7": ffn,
         "measured_peaks": {"bf16_mfma_tflops": mfma_peak, "copy_gbs": copy_peak,
