@@ -134,14 +134,28 @@ __global__ __launch_bounds__(kSumWaves * kWave) void block_sum_kernel(
   const float* rl = row_lse + (int64_t)r * rows;
   float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
   if (ne == n && (rows & 3) == 0) {
-    // every window row is valid: 4 rows per lane per step
-    for (int row = 4 * lane; row < rows; row += 4 * kWave) {
-      const floatx4 v = *reinterpret_cast<const floatx4*>(src + row);
-      const floatx4 l = *reinterpret_cast<const floatx4*>(rl + row);
-      acc0 += __builtin_amdgcn_exp2f(v[0] - l[0]);
-      acc1 += __builtin_amdgcn_exp2f(v[1] - l[1]);
-      acc2 += __builtin_amdgcn_exp2f(v[2] - l[2]);
-      acc3 += __builtin_amdgcn_exp2f(v[3] - l[3]);
+    // every window row is valid: 4 rows per lane per step, eight steps' loads
+    // in flight before their exponentials
+    constexpr int kSteps = 8;
+    for (int base = 4 * lane; base < rows; base += 4 * kWave * kSteps) {
+      floatx4 v[kSteps], l[kSteps];
+#pragma unroll
+      for (int u = 0; u < kSteps; ++u) {
+        const int row = base + u * 4 * kWave;
+        if (row < rows) {
+          v[u] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(src + row));
+          l[u] = *reinterpret_cast<const floatx4*>(rl + row);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kSteps; ++u) {
+        if (base + u * 4 * kWave < rows) {
+          acc0 += __builtin_amdgcn_exp2f(v[u][0] - l[u][0]);
+          acc1 += __builtin_amdgcn_exp2f(v[u][1] - l[u][1]);
+          acc2 += __builtin_amdgcn_exp2f(v[u][2] - l[u][2]);
+          acc3 += __builtin_amdgcn_exp2f(v[u][3] - l[u][3]);
+        }
+      }
     }
   } else {
     for (int row = lane; row < rows; row += kWave)

@@ -149,6 +149,8 @@ up_status up_ffn_forward(up_ffn* f, const void* x, int64_t rows, const void* w_g
     return UP_ERR_NULL;
   if (((uintptr_t)x | (uintptr_t)w_gate_up | (uintptr_t)w_down | (uintptr_t)y | (uintptr_t)workspace) % 16 != 0)
     return UP_ERR_ALIGN;
+  // the activation kernel's grid (eight channels per thread) must fit 32 bits
+  if (rows > (int64_t)UINT32_MAX / (f->F / 8) * up::kSwigluThreads / 2) return UP_ERR_SHAPE;
   if (workspace_bytes < up_ffn_workspace_bytes(f, rows)) return UP_ERR_WORKSPACE;
   const int64_t D = f->D, F = f->F;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
