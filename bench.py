@@ -245,6 +245,39 @@ def ratio(a, b):
     return None if b is None else a / b
 
 
+def run_sweep(args, ev, stream):
+    """The step on every workload shape of the parity suite (short to long
+    contexts, one to sixteen requests); prints one JSON line with a record per
+    workload.  Not the benchmark line: the 128K request is the measured
+    configuration."""
+    import torch
+    import synth
+    wls = [synth.llama_4k(), synth.llama_varlen4(), synth.hybrid_64k("qwen_next", 64),
+           synth.hybrid_64k("gemma3", 64, p=0.98), synth.llama_128k(), synth.serving_16x128k()]
+    records = []
+    for wl in wls:
+        log(f"[sweep] {wl.name}: {wl.num_reqs} request(s), {sum(wl.lengths)} tokens")
+        m = measure_step(wl, args.steps, args.warmup, ev, stream)
+        T = m["T"]
+        flops = sum(2.0 * min(wl.n, L) * wl.hq * wl.d * L for L in wl.lengths)
+        rec = {"workload": wl.name, "requests": m["R"], "tokens": T, "kept": m["kept"],
+               "num_heads_q": wl.hq, "num_heads_kv": wl.hkv, "head_dim": wl.d, "hidden": wl.hidden,
+               "G": wl.G, "p": wl.p, "ms_per_step": m["ms_per_step"],
+               "launch": "hip_graph" if m["ms_graph"] is not None else "eager",
+               "tokens_per_s": T / (m["ms_per_step"] * 1e-3),
+               "breakdown_ms": {"select": m["select_ms"], "score_kernel": m["score_ms"],
+                                "compact": m["compact_ms"], "metadata": m["meta_ms"],
+                                "scatter_back": m["scatter_ms"]},
+               "score_tflops": flops / (m["score_ms"] * 1e-3) / 1e12}
+        log(f"[sweep] {wl.name}: {rec['ms_per_step']:.3f} ms/step ({rec['launch']}), "
+            f"{rec['tokens_per_s'] / 1e6:.1f} M tokens/s, score {m['score_ms'] * 1e3:.1f} us "
+            f"({rec['score_tflops']:.0f} TFLOP/s), kept {m['kept']}/{T}")
+        records.append(rec)
+        del m
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": records}), flush=True)
+
+
 def threads_used():
     n = len(os.sched_getaffinity(0))
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
@@ -254,45 +287,20 @@ def threads_used():
     return n
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--step-only", action="store_true",
-                    help="time the step only: skip the next-row extras (Eq. 16 slots and KV write, the FFN) "
-                         "and the measured peaks (for short profiled runs)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures the single-GPU hot path only; --gpus {args.gpus} is not supported "
-              "(nothing in this path spans GPUs).", file=sys.stderr)
-        sys.exit(2)
-
+def measure_step(wl, steps, warmup, ev, stream):
+    """Set up one workload (seeded inputs resident in HBM) and time the step:
+    eager, eager with per-phase events (breakdown), and replayed from a HIP
+    graph after three bit-exact checks against the eager step."""
     import numpy as np
     import torch
-
     import synth
     import token_level_block_amd as tlb
     from token_level_block_amd.runner import CompactBuffers, MetadataBuffers, SelectBuffers, run_scatter_back
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    torch.cuda.set_device(0)
-
-    if args.copy_calibration:
-        src = torch.ones(1 << 28, dtype=torch.int32, device="cuda")   # 1 GiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] copied {src.numel() * 4} bytes three times")
-        return
-
-    wl = synth.llama_128k()
+    class _A:
+        pass
+    args = _A()
+    args.steps, args.warmup = steps, warmup
     log(f"[bench] generating {wl.name}: lengths={wl.lengths} hq={wl.hq} hkv={wl.hkv} d={wl.d} D={wl.hidden}")
     cu, q, k = synth.make_qk(wl)
     T = int(cu[-1])
@@ -313,8 +321,6 @@ def main():
     sel = SelectBuffers.allocate(prm, R, T)
     cb = CompactBuffers.allocate(R, T)
     mb = MetadataBuffers.allocate(np.diff(cu), num_layers=32, max_drops=4)
-    stream = torch.cuda.current_stream().cuda_stream
-    ev = HipEvents()
 
     def step(s, marks=None):
         if marks is not None:
@@ -404,6 +410,64 @@ def main():
     scatter_ms = mean("t3", "t4")
 
     kept = int(sel.kept[:R].sum().item())
+    return dict(wl=wl, T=T, R=R, kept=kept, cu=cu, q=q, k=k, cu_d=cu_d, sel=sel, cb=cb, nwords=nwords,
+                ms_eager=ms_eager, ms_graph=ms_graph, graph_note=graph_note, ms_per_step=ms_per_step,
+                score_ms=score_ms, select_ms=select_ms, compact_ms=compact_ms, meta_ms=meta_ms,
+                scatter_ms=scatter_ms, release=lambda: None)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step only: skip the next-row extras (Eq. 16 slots and KV write, the FFN) "
+                         "and the measured peaks (for short profiled runs)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the step on every workload shape (4K to 16 x 128K) instead of the benchmark line")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures the single-GPU hot path only; --gpus {args.gpus} is not supported "
+              "(nothing in this path spans GPUs).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import token_level_block_amd as tlb
+    from token_level_block_amd.runner import CompactBuffers, MetadataBuffers, SelectBuffers, run_scatter_back
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.int32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {src.numel() * 4} bytes three times")
+        return
+
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents()
+    if args.sweep:
+        run_sweep(args, ev, stream)
+        return
+    wl = synth.llama_128k()
+    m = measure_step(wl, args.steps, args.warmup, ev, stream)
+    T, R, kept, cu, q, k, cu_d, sel, cb, nwords = (m[x] for x in ("T", "R", "kept", "cu", "q", "k", "cu_d", "sel",
+                                                                    "cb", "nwords"))
+    ms_eager, ms_graph, graph_note, ms_per_step = m["ms_eager"], m["ms_graph"], m["graph_note"], m["ms_per_step"]
+    score_ms, select_ms, compact_ms = m["score_ms"], m["select_ms"], m["compact_ms"]
+    meta_ms, scatter_ms = m["meta_ms"], m["scatter_ms"]
     keep_ratio = kept / T
     tokens_per_s = T / (ms_per_step * 1e-3)
     sel_compact_tps = T / ((select_ms + compact_ms + meta_ms) * 1e-3)
@@ -424,7 +488,6 @@ def main():
     nblocks = int(sel.block_offsets[R].item())
     sc_bytes = 2 * kept * row_bytes + 4 * kept + T + 5 * nblocks
     sc_gbs = sc_bytes / ((select_ms + compact_ms) * 1e-3) / 1e9
-    del qd, kd, hidden, out, full
     torch.cuda.empty_cache()
     kv = ffn = None
     mfma_peak = copy_peak = None

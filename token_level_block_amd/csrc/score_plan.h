@@ -12,10 +12,10 @@ namespace up {
 // per resident slot: 256 CUs, one 8-wave workgroup per CU at the score
 // kernel's register use (two 4-wave ones when a KV head has at most 256
 // window queries).  The length is a multiple of G (so no G-block straddles two
-// workgroups), at least the multiple of G nearest 1024 from below (or G) and
-// at most 8192 keys.
+// workgroups), between the multiple of G nearest 128 from above (one LDS stage:
+// short batches still fill the chip) and 8192 keys.
 inline int32_t chunk_keys_for(int32_t G, int32_t hq, int32_t hkv, int32_t n, int64_t max_tokens) {
-  const int32_t base = G >= 1024 ? G : G * (1024 / G);
+  const int32_t base = G >= 128 ? G : G * ((128 + G - 1) / G);
   if (hkv < 1 || hq < hkv || n < 1) return base;
   const int64_t qn = (int64_t)(hq / hkv) * n;
   const int64_t zsplit = qn <= 256 ? 1 : (qn + 511) / 512;
