@@ -20,6 +20,7 @@
 // Keys after a window row's own position are masked (causal masking), as
 // are keys past the end of the request.
 #include "common.h"
+#include "score_plan.h"
 
 namespace up {
 
@@ -27,10 +28,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int D, int NW>
+template <int D, int NW, int NT_>
 struct ScoreCfg {
   static constexpr int KSTEPS = D / 16;              // MFMA k-steps per 32-key tile
-  static constexpr int NT = 2;                       // 32-query column tiles per wave
+  static constexpr int NT = NT_;                     // 32-query column tiles per wave
   static constexpr int QW = 32 * NT;                 // queries per wave
   static constexpr int KT = (D <= 128) ? 128 : 64;   // keys per LDS stage
   static constexpr int SUB = KT / 32;                // 32-key tiles per stage
@@ -86,9 +87,9 @@ constexpr float kRescaleAbove = 1048576.0f;   // 2^20
 
 // GT = G/32 tiles per block when G is 32, 64 or 128 (block ends known at
 // compile time in the plain stages), 0 for any other multiple of 32.
-template <int D, int NW, int GT>
+template <int D, int NW, int GT, int NT>
 __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
-  using C = ScoreCfg<D, NW>;
+  using C = ScoreCfg<D, NW, NT>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
 
   const int gc = blockIdx.x;
@@ -293,17 +294,18 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
 
 template <int D, int GT>
 static hipError_t launch_score_dg(const ScoreArgs& a, hipStream_t s) {
-  // 4 waves when the KV head's window queries fit in 256 columns, else 8 waves
-  // and as many query slices (grid z) as needed
-  const int qn = (a.hq / a.hkv) * a.n;
-  if (qn <= 4 * 64) {
-    dim3 grid((unsigned)a.max_chunks, (unsigned)a.hkv, 1u);
-    hipLaunchKernelGGL((score_kernel<D, 4, GT>), grid, dim3(4 * kWave), 0, s, a);
-  } else {
-    const int zsplit = (qn + 8 * 64 - 1) / (8 * 64);
-    dim3 grid((unsigned)a.max_chunks, (unsigned)a.hkv, (unsigned)zsplit);
-    hipLaunchKernelGGL((score_kernel<D, 8, GT>), grid, dim3(8 * kWave), 0, s, a);
+  const ScoreLaunch L = score_launch_for(a.d, a.hq, a.hkv, a.n);
+  const dim3 grid((unsigned)a.max_chunks, (unsigned)a.hkv, (unsigned)L.zsplit);
+  if constexpr (D > 128) {
+    if (L.nt == 1) {
+      hipLaunchKernelGGL((score_kernel<D, 8, GT, 1>), grid, dim3(8 * kWave), 0, s, a);
+      return hipGetLastError();
+    }
   }
+  if (L.nw == 4)
+    hipLaunchKernelGGL((score_kernel<D, 4, GT, 2>), grid, dim3(4 * kWave), 0, s, a);
+  else
+    hipLaunchKernelGGL((score_kernel<D, 8, GT, 2>), grid, dim3(8 * kWave), 0, s, a);
   return hipGetLastError();
 }
 

@@ -6,21 +6,37 @@
 
 namespace up {
 
+// Launch shape of the score kernel for one KV head's qn = (Hq/Hkv)*n window
+// queries: waves per workgroup, 32-query column tiles per wave, query slices
+// (grid z), and how many such workgroups one CU holds at the kernel's
+// register use.  Two column tiles per wave halve the LDS reads per MFMA;
+// at d = 256 with at most 256 queries that would leave one wave per SIMD
+// (query fragments and accumulators of two tiles at d = 256 take 260
+// registers), so that case uses one tile per wave and eight waves.
+struct ScoreLaunch {
+  int nw, nt, zsplit, per_cu;
+};
+
+inline ScoreLaunch score_launch_for(int32_t d, int32_t hq, int32_t hkv, int32_t n) {
+  const int64_t qn = (int64_t)(hq / hkv) * n;
+  if (d > 128 && qn <= 256) return {8, 1, 1, 1};
+  if (qn <= 256) return {4, 2, 1, 2};
+  return {8, 2, (int)((qn + 511) / 512), 1};
+}
+
 // Keys per score workgroup.  A workgroup pays a fixed start-up (its query
 // fragments and first K stage arrive before any MFMA can issue), so chunks are
 // made as long as possible while one launch still offers about one workgroup
-// per resident slot: 256 CUs, one 8-wave workgroup per CU at the score
-// kernel's register use (two 4-wave ones when a KV head has at most 256
-// window queries).  The length is a multiple of G (so no G-block straddles two
-// workgroups), between the multiple of G nearest 128 from above (one LDS stage:
-// short batches still fill the chip) and 8192 keys.
-inline int32_t chunk_keys_for(int32_t G, int32_t hq, int32_t hkv, int32_t n, int64_t max_tokens) {
+// per resident slot (256 CUs times the workgroups a CU holds).  The length is
+// a multiple of G (so no G-block straddles two workgroups), between the
+// multiple of G nearest 128 from above (one LDS stage: short batches still
+// fill the chip) and 8192 keys.
+inline int32_t chunk_keys_for(int32_t G, int32_t d, int32_t hq, int32_t hkv, int32_t n, int64_t max_tokens) {
   const int32_t base = G >= 128 ? G : G * ((128 + G - 1) / G);
   if (hkv < 1 || hq < hkv || n < 1) return base;
-  const int64_t qn = (int64_t)(hq / hkv) * n;
-  const int64_t zsplit = qn <= 256 ? 1 : (qn + 511) / 512;
-  const int64_t slots = qn <= 256 ? 512 : 256;
-  const int64_t want = (max_tokens * hkv * zsplit + slots - 1) / slots;
+  const ScoreLaunch L = score_launch_for(d, hq, hkv, n);
+  const int64_t slots = 256 * (int64_t)L.per_cu;
+  const int64_t want = (max_tokens * hkv * L.zsplit + slots - 1) / slots;
   const int64_t cap = base > 8192 ? base : 8192;
   int64_t ck = (want + base - 1) / base * base;
   if (ck < base) ck = base;
