@@ -3,9 +3,9 @@
 
 One step = one full-attention layer's pass over the hot path on the resident
 workload: up_select_blocks (score GEMM + online softmax + block reduce, top-p,
-expansion), up_compact of the hidden rows, up_update_metadata, and the Eq. 8
-up_scatter_back.  The workload is one 131072-token request shaped like a
-LLaMA-3.1-8B full-attention layer (32 query heads, 8 KV heads, head_dim 128,
+expansion), up_compact of the hidden rows and token positions,
+up_update_metadata, and the Eq. 8 up_scatter_back of the hidden rows.  The
+workload is one 131072-token request shaped like a LLaMA-3.1-8B full-attention layer (32 query heads, 8 KV heads, head_dim 128,
 hidden 4096, bf16), seeded synthetic data (synth.llama_128k).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -316,6 +316,10 @@ def measure_step(wl, steps, warmup, ev, stream):
     hidden = synth.hidden_words_torch(0, T, nwords, "cuda")
     out = torch.empty_like(hidden)
     full = hidden.clone()
+    # token positions (RoPE) move with the hidden rows: position within the request
+    owner = torch.repeat_interleave(torch.arange(R, device="cuda"), cu_d[1:].long() - cu_d[:-1].long())
+    pos = (torch.arange(T, device="cuda") - cu_d[:-1].long()[owner]).to(torch.int32)
+    pos_out = torch.empty_like(pos)
 
     prm = tlb.make_params(wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p)
     sel = SelectBuffers.allocate(prm, R, T)
@@ -331,7 +335,7 @@ def measure_step(wl, steps, warmup, ev, stream):
         sel.run(qd, kd, cu_d, stream=s)
         if marks is not None:
             ev.record(marks["t1"], s)
-        cb.run(sel.keep_mask, cu_d, [hidden], [out], stream=s)
+        cb.run(sel.keep_mask, cu_d, [hidden, pos], [out, pos_out], stream=s)
         if marks is not None:
             ev.record(marks["t2"], s)
         mb.run(0, cu_d, cb.cu_out, stream=s)
@@ -359,7 +363,8 @@ def measure_step(wl, steps, warmup, ev, stream):
     kept_now = int(cb.cu_out[R].item())
 
     def live():
-        return (sel.keep_mask[:T], sel.kept[:R], cb.cu_out, cb.index_out[:kept_now], out[:kept_now], full)
+        return (sel.keep_mask[:T], sel.kept[:R], cb.cu_out, cb.index_out[:kept_now], out[:kept_now],
+                pos_out[:kept_now], full)
     ref_out = [t.clone() for t in live()]
     # ... K more with events between the phases, for the per-kernel breakdown
     marks = [dict(score=(ev.new(), ev.new()), t0=ev.new(), t1=ev.new(), t2=ev.new(), t3=ev.new(), t4=ev.new())
@@ -385,10 +390,10 @@ def measure_step(wl, steps, warmup, ev, stream):
             step(torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
         for _ in range(3):
-            for t in (sel.keep_mask, out):
+            for t in (sel.keep_mask, out, pos_out):
                 t.zero_()
             step(stream)                 # eager work between replays
-            for t in (sel.keep_mask, out):
+            for t in (sel.keep_mask, out, pos_out):
                 t.zero_()
             graph.replay()
             torch.cuda.synchronize()
@@ -475,7 +480,7 @@ def main():
     flops = 2.0 * wl.n * wl.hq * wl.d * T
     score_tflops = flops / (score_ms * 1e-3) / 1e12
     row_bytes = wl.hidden * 2
-    compact_bytes = 2 * kept * row_bytes + 4 * kept + T
+    compact_bytes = 2 * kept * row_bytes + 2 * 4 * kept + 4 * kept + T   # hidden and position rows, index map, mask
     compact_gbs = compact_bytes / (compact_ms * 1e-3) / 1e9
     scatter_bytes = 2 * kept * row_bytes + 4 * kept
     scatter_gbs = scatter_bytes / (scatter_ms * 1e-3) / 1e9
@@ -486,7 +491,7 @@ def main():
     # select + compact as HBM work (the score GEMM's K reads are counted under MFMA):
     # kept rows read and written, index map, token mask, block scores and flags
     nblocks = int(sel.block_offsets[R].item())
-    sc_bytes = 2 * kept * row_bytes + 4 * kept + T + 5 * nblocks
+    sc_bytes = 2 * kept * row_bytes + 2 * 4 * kept + 4 * kept + T + 5 * nblocks
     sc_gbs = sc_bytes / ((select_ms + compact_ms) * 1e-3) / 1e9
     torch.cuda.empty_cache()
     kv = ffn = None

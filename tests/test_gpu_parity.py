@@ -174,6 +174,7 @@ COMPACT_CASES = [
     (3, tuple([4100] * 5), 0.9, (7680, 4096)),
     (4, (300, 0), 0.0, (32,)),
     (5, (70000,), 1.0, (4,)),
+    (6, (777, 0, 1234), 0.5, (36, 48, 100, 16)),   # wide unaligned rows, 3-unit rows, narrow aligned rows
 ]
 
 

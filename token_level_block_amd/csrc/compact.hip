@@ -158,10 +158,11 @@ __global__ __launch_bounds__(kGatherThreads) void rank_kernel(CompactArgs a) {
 // two rows per trip, up to sixteen 16-byte nontemporal loads in flight per lane
 // (the rows are streamed once, so they bypass cache residency).  Equal ranges
 // keep the last trip from running on a fraction of the waves.  4-byte path:
-// rows dealt round-robin, one per trip.
+// rows of at most 32 bytes one per thread, wider rows one per wave trip.
 // ---------------------------------------------------------------------------
 constexpr int kCopyThreads = 256;
 constexpr int kCopyWaves = kCopyThreads / kWave;
+constexpr int64_t kNarrowRow = 32;   // rows up to this many bytes (not 16-byte aligned) go one per thread
 
 template <bool kGather>
 __device__ __forceinline__ void row_ends(const int32_t* __restrict__ map, int64_t k, int64_t& s, int64_t& d) {
@@ -214,6 +215,19 @@ __global__ __launch_bounds__(kCopyThreads) void copy_rows_kernel(const uint8_t* 
         }
       }
     }
+  } else if (rb <= kNarrowRow) {
+    // narrow rows (positions, indices): one thread per row
+    const int64_t t = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+    const int64_t T = (int64_t)gridDim.x * kCopyThreads;
+    const int units = (int)(rb >> 2);
+    for (int64_t k = t; k < count; k += T) {
+      int64_t s, d;
+      row_ends<kGather>(map, k, s, d);
+      if (d < 0 || d >= dst_rows) continue;
+      const uint32_t* sp = reinterpret_cast<const uint32_t*>(src + s * rb);
+      uint32_t* dp = reinterpret_cast<uint32_t*>(dst + d * rb);
+      for (int u = 0; u < units; ++u) dp[u] = sp[u];
+    }
   } else {
     for (int64_t k = gw; k < count; k += W) {
       int64_t s, d;
@@ -237,6 +251,7 @@ static hipError_t launch_copy(bool gather, bool vec, const uint8_t* src, uint8_t
                               const int32_t* map, const int32_t* count_ptr, int64_t max_rows,
                               int64_t dst_rows, hipStream_t s) {
   const dim3 grid(copy_grid(max_rows)), block(kCopyThreads);
+  if (rb <= kNarrowRow) vec = false;   // one thread per row beats a wave per row
   if (gather && vec)
     hipLaunchKernelGGL((copy_rows_kernel<true, true>), grid, block, 0, s, src, dst, rb, map, count_ptr, max_rows, dst_rows);
   else if (gather)
