@@ -198,11 +198,10 @@ up_status up_select_blocks(const up_select_params* prm, const void* q, int64_t q
 
 size_t up_compact_workspace_bytes(int32_t num_reqs, int64_t max_tokens) {
   if (num_reqs < 0 || max_tokens < 0 || max_tokens > INT32_MAX) return 0;
+  // per-4096-token counts, then the stream position of each kept row
   const int64_t ntiles = (max_tokens + up::kCountTile - 1) / up::kCountTile;
-  size_t off = align_up(sizeof(int32_t) * (size_t)(num_reqs + 1));
-  off = align_up(off + sizeof(int32_t) * (size_t)ntiles);
-  off = align_up(off + sizeof(int32_t) * (size_t)(ntiles + 1));
-  off = align_up(off + sizeof(int32_t) * (size_t)max_tokens);
+  size_t off = align_up(sizeof(int32_t) * (size_t)(ntiles > 0 ? ntiles : 1));
+  off = align_up(off + sizeof(int32_t) * (size_t)(max_tokens > 0 ? max_tokens : 1));
   return off;
 }
 
@@ -234,14 +233,8 @@ up_status up_compact(const uint8_t* keep_mask, const int32_t* cu_seqlens, int32_
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int64_t ntiles = (max_tokens + up::kCountTile - 1) / up::kCountTile;
-  size_t off = 0;
-  a.cu_s = reinterpret_cast<int32_t*>(ws + off);
-  off = align_up(off + sizeof(int32_t) * (size_t)(num_reqs + 1));
-  a.tile_count = reinterpret_cast<int32_t*>(ws + off);
-  off = align_up(off + sizeof(int32_t) * (size_t)ntiles);
-  a.tile_prefix = reinterpret_cast<int32_t*>(ws + off);
-  off = align_up(off + sizeof(int32_t) * (size_t)(ntiles + 1));
-  a.src_pos = reinterpret_cast<int32_t*>(ws + off);
+  a.tile_count = reinterpret_cast<int32_t*>(ws);
+  a.src_pos = reinterpret_cast<int32_t*>(ws + align_up(sizeof(int32_t) * (size_t)(ntiles > 0 ? ntiles : 1)));
   a.num_count_tiles = ntiles;
   a.mask = keep_mask;
   a.cu_in = cu_seqlens;

@@ -88,9 +88,7 @@ struct CompactArgs {
   int32_t* index_out;
   int32_t* cu_out;
   // workspace
-  int32_t* cu_s;          // [R+1]
   int32_t* tile_count;    // [num_count_tiles]
-  int32_t* tile_prefix;   // [num_count_tiles + 1]
   int32_t* src_pos;       // [max_tokens] stream position of each kept row
   int64_t num_count_tiles;
 };

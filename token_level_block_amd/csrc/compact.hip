@@ -3,11 +3,11 @@
 // patched query_start_loc describes).
 //
 //   count  : one workgroup per 4096-token tile counts the set mask bytes;
-//   scan   : one workgroup clamps cu_seqlens and turns the tile counts into
-//            exclusive prefixes;
-//   rank   : one workgroup per 256-token tile ranks its kept tokens (wave
-//            ballots) and writes the index map, the stream position of every
-//            kept row and the new request offsets that fall in its tile;
+//   rank   : one workgroup per 256-token tile adds up the counts before it,
+//            ranks its kept tokens (wave ballots) and writes the index map,
+//            the stream position of every kept row and the new request
+//            offsets (of the clamped, non-decreasing cu_seqlens) that fall in
+//            its tile;
 //   copy   : waves spread evenly over the kept rows copy each row of every
 //            buffer with coalesced 16-byte accesses (the same kernel moves the
 //            rows back for the Eq. 8 scatter).
@@ -18,7 +18,6 @@ namespace up {
 
 constexpr int kCountThreads = kCountTile / 16;   // 16 mask bytes per thread
 constexpr int kGatherThreads = kGatherTile;      // one token per thread
-constexpr int kScanThreads = 1024;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -55,73 +54,61 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(const uint8_t* __r
   }
 }
 
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ cu_in, int R,
-                                                            int64_t max_tokens,
-                                                            const int32_t* __restrict__ tile_count,
-                                                            int64_t ntiles, int32_t* __restrict__ cu_s,
-                                                            int32_t* __restrict__ tile_prefix,
-                                                            int32_t* __restrict__ cu_out) {
-  __shared__ int32_t scratch[kScanThreads / kWave];
-  __shared__ int32_t carry;
-  const int tid = threadIdx.x;
-  const int32_t cap = (int32_t)(max_tokens < 0x7fffffff ? max_tokens : 0x7fffffff);
-  if (tid == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base <= R; base += kScanThreads) {
-    const int e = base + tid;
-    const int32_t v = (e <= R) ? max(0, min(cu_in[e], cap)) : 0;
-    const int32_t m = max(block_inclusive_scan<true>(v, scratch), carry);
-    if (e <= R) cu_s[e] = m;
-    __syncthreads();
-    if (tid == kScanThreads - 1) carry = m;
-    __syncthreads();
-  }
-  const int32_t T = carry;
-  if (tid == 0) carry = 0;
-  __syncthreads();
-  for (int64_t base = 0; base < ntiles; base += kScanThreads) {
-    const int64_t t = base + tid;
-    const int32_t v = (t < ntiles) ? tile_count[t] : 0;
-    const int32_t incl = block_inclusive_scan<false>(v, scratch) + carry;
-    if (t < ntiles) tile_prefix[t] = incl - v;
-    if (t == ntiles - 1) tile_prefix[ntiles] = incl;
-    __syncthreads();
-    if (tid == kScanThreads - 1) carry = incl;
-    __syncthreads();
-  }
-  // an empty stream has no gather tile to report the request offsets
-  if (T == 0)
-    for (int e = tid; e <= R; e += kScanThreads) cu_out[e] = 0;
-}
+// clamp(cu[e]) into [0, cap]; the running maximum of these is the clamped,
+// non-decreasing offset array every kernel here works with
+__device__ __forceinline__ int32_t clamp_cu(int32_t v, int32_t cap) { return max(0, min(v, cap)); }
 
 __global__ __launch_bounds__(kGatherThreads) void rank_kernel(CompactArgs a) {
   __shared__ int32_t red[kGatherThreads / kWave];
   __shared__ int32_t wsum[kGatherThreads / kWave];
   __shared__ int32_t excl[kGatherThreads + 1];
-  __shared__ int32_t s_prefix;
+  __shared__ int32_t s_T, s_prefix, s_carry;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int32_t cap = (int32_t)(a.max_tokens < 0x7fffffff ? a.max_tokens : 0x7fffffff);
+  const int R = a.R;
+
+  // stream length T = the last clamped offset = the largest clamped entry
+  int32_t m = 0;
+  for (int e = tid; e <= R; e += kGatherThreads) m = max(m, clamp_cu(a.cu_in[e], cap));
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o));
+  if (lane == 0) red[wid] = m;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t t = 0;
+    for (int w = 0; w < kGatherThreads / kWave; ++w) t = max(t, red[w]);
+    s_T = t;
+  }
+  __syncthreads();
+  const int32_t T = s_T;
   const int64_t start = (int64_t)blockIdx.x * kGatherTile;
-  const int32_t T = a.cu_s[a.R];
+  if (T == 0) {
+    // an empty stream has no tile to report the request offsets
+    if (blockIdx.x == 0)
+      for (int e = tid; e <= R; e += kGatherThreads) a.cu_out[e] = 0;
+    return;
+  }
   if (start >= T) return;
   const int64_t end = min<int64_t>(start + kGatherTile, T);
 
-  // kept tokens before this tile: the count tile's prefix plus the pieces of
-  // the count tile that precede this tile
+  // kept tokens before this tile: whole count tiles before it, plus the pieces
+  // of its own count tile that precede it
   const int64_t ct = start / kCountTile;
   const int64_t cstart = ct * kCountTile;
   int c = 0;
+  for (int64_t t = tid; t < ct; t += kGatherThreads) c += a.tile_count[t];
   {
     const int64_t pos = cstart + (int64_t)tid * 16;
-    if (pos < start) c = count_piece(a.mask, pos, start);
+    if (pos < start) c += count_piece(a.mask, pos, start);
   }
   for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
   if (lane == 0) red[wid] = c;
   __syncthreads();
   if (tid == 0) {
-    int t = a.tile_prefix[ct];
+    int t = 0;
     for (int w = 0; w < kGatherThreads / kWave; ++w) t += red[w];
     s_prefix = t;
+    s_carry = 0;
   }
 
   const int64_t i = start + tid;
@@ -142,11 +129,16 @@ __global__ __launch_bounds__(kGatherThreads) void rank_kernel(CompactArgs a) {
     a.index_out[prefix + local] = a.index_in ? a.index_in[i] : (int32_t)i;
     a.src_pos[prefix + local] = (int32_t)i;
   }
-  // new request offsets that fall inside this tile (the last tile also owns position T)
-  for (int r = tid; r <= a.R; r += kGatherThreads) {
-    const int32_t p = a.cu_s[r];
-    if (p >= start && (p < end || (p == T && end == T)))
-      a.cu_out[r] = prefix + excl[p - start];
+  // new request offsets that fall inside this tile (the last tile also owns
+  // position T): the clamped running maximum of cu, a chunk at a time
+  for (int base = 0; base <= R; base += kGatherThreads) {
+    const int e = base + tid;
+    const int32_t v = (e <= R) ? clamp_cu(a.cu_in[e], cap) : 0;
+    const int32_t p = max(block_inclusive_scan<true>(v, red), s_carry);
+    if (e <= R && p >= start && (p < end || (p == T && end == T))) a.cu_out[e] = prefix + excl[p - start];
+    __syncthreads();
+    if (tid == kGatherThreads - 1) s_carry = p;
+    __syncthreads();
   }
 }
 
@@ -270,16 +262,10 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a.cu_in, (int)a.R, a.max_tokens,
-                     a.tile_count, a.num_count_tiles, a.cu_s, a.tile_prefix, a.cu_out);
+  const int64_t ntiles = (a.max_tokens + kGatherTile - 1) / kGatherTile;
+  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)(ntiles > 0 ? ntiles : 1)), dim3(kGatherThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t ntiles = (a.max_tokens + kGatherTile - 1) / kGatherTile;
-  if (ntiles > 0) {
-    hipLaunchKernelGGL(rank_kernel, dim3((unsigned)ntiles), dim3(kGatherThreads), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   for (int b = 0; b < a.bufs.nbuf; ++b) {
     e = launch_copy(true, a.bufs.vec16[b] != 0, a.bufs.src[b], a.bufs.dst[b], a.bufs.row_bytes[b], a.src_pos,
                     a.cu_out + a.R, a.max_tokens, a.max_tokens, s);
