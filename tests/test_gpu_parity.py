@@ -464,3 +464,33 @@ def test_window_ablation_sizes(n):
         [synth.RequestStructure("powerlaw", c=synth.POWERLAW_C)] * 2)
     ref, got, mism = check_select(wl)
     say(f"  n={n}: kept={got['kept'].tolist()} mismatched={mism}")
+
+
+# ---------------------------------------------------------------------------
+# Q and K as views into one fused QKV projection buffer (the layout serving
+# stacks hand over): row strides larger than Hq*d and Hkv*d
+# ---------------------------------------------------------------------------
+def test_select_fused_qkv_views():
+    wl = synth.tiny((700, 1500, 90), hq=8, hkv=2, d=128, G=64, A=64, n=64, p=0.95, seed=17,
+                    kind="hot", hot=3, hot_lambda=6.0)
+    cu, q, k = synth.make_qk(wl)
+    T = int(cu[-1])
+    ref_contig = run_select(wl, cu, q, k)
+    width = (wl.hq + 2 * wl.hkv) * wl.d
+    qkv = torch.full((T, width), 0x7F80, dtype=torch.int16, device="cuda")   # bf16 +inf outside Q and K
+    cu_d, qd, kd = upload_qk(wl, cu, q, k)
+    qkv[:, : wl.hq * wl.d] = qd.reshape(T, -1)
+    qkv[:, wl.hq * wl.d: (wl.hq + wl.hkv) * wl.d] = kd.reshape(T, -1)
+    qv = qkv[:, : wl.hq * wl.d]
+    kv = qkv[:, wl.hq * wl.d: (wl.hq + wl.hkv) * wl.d]
+    assert qv.stride(0) == width and kv.stride(0) == width
+    prm = tlb.make_params(wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p)
+    bufs = SelectBuffers.allocate(prm, wl.num_reqs, T)
+    bufs.run(qv, kv, cu_d)
+    torch.cuda.synchronize()
+    nbt = int(ref_contig["offs"][-1])
+    assert np.array_equal(bufs.block_scores[:nbt].cpu().numpy(), ref_contig["b"])
+    assert np.array_equal(bufs.keep_mask[:T].cpu().numpy(), ref_contig["mask"])
+    assert np.array_equal(bufs.kept[: wl.num_reqs].cpu().numpy(), ref_contig["kept"])
+    ref = oracle.select(q, k, cu, wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p)
+    check_scores(ref_contig["b"], ref["b64"], ref["block_offsets"])
