@@ -162,17 +162,23 @@ __device__ __forceinline__ void row_ends(const int32_t* __restrict__ map, int64_
   d = kGather ? k : (int64_t)map[k];
 }
 
-template <bool kGather, bool kVec>
-__global__ __launch_bounds__(kCopyThreads) void copy_rows_kernel(const uint8_t* __restrict__ src,
-                                                                 uint8_t* __restrict__ dst, int64_t rb,
+// One launch moves every buffer: grid row y copies buffer y.  The path is
+// chosen per buffer (uniform over a workgroup): 16-byte rows wider than 32
+// bytes, narrow rows, or other 4-byte rows.
+template <bool kGather>
+__global__ __launch_bounds__(kCopyThreads) void copy_rows_kernel(RowBuffers bufs,
                                                                  const int32_t* __restrict__ map,
                                                                  const int32_t* __restrict__ count_ptr,
                                                                  int64_t max_rows, int64_t dst_rows) {
+  const int b = blockIdx.y;
+  const uint8_t* __restrict__ src = bufs.src[b];
+  uint8_t* __restrict__ dst = bufs.dst[b];
+  const int64_t rb = bufs.row_bytes[b];
   const int lane = threadIdx.x & 63;
   const int64_t gw = (int64_t)blockIdx.x * kCopyWaves + (threadIdx.x >> 6);
   const int64_t W = (int64_t)gridDim.x * kCopyWaves;
   const int64_t count = min<int64_t>(*count_ptr, max_rows);
-  if (kVec) {
+  if (bufs.vec16[b] != 0 && rb > kNarrowRow) {
     const int64_t per = (((count + W - 1) / W) + 1) & ~(int64_t)1;
     const int64_t k0 = gw * per, k1 = min<int64_t>(count, k0 + per);
     const int units = (int)(rb >> 4);
@@ -239,19 +245,14 @@ static unsigned copy_grid(int64_t max_rows) {
   return (unsigned)(want < 1 ? 1 : (want > 4096 ? 4096 : want));
 }
 
-static hipError_t launch_copy(bool gather, bool vec, const uint8_t* src, uint8_t* dst, int64_t rb,
-                              const int32_t* map, const int32_t* count_ptr, int64_t max_rows,
-                              int64_t dst_rows, hipStream_t s) {
-  const dim3 grid(copy_grid(max_rows)), block(kCopyThreads);
-  if (rb <= kNarrowRow) vec = false;   // one thread per row beats a wave per row
-  if (gather && vec)
-    hipLaunchKernelGGL((copy_rows_kernel<true, true>), grid, block, 0, s, src, dst, rb, map, count_ptr, max_rows, dst_rows);
-  else if (gather)
-    hipLaunchKernelGGL((copy_rows_kernel<true, false>), grid, block, 0, s, src, dst, rb, map, count_ptr, max_rows, dst_rows);
-  else if (vec)
-    hipLaunchKernelGGL((copy_rows_kernel<false, true>), grid, block, 0, s, src, dst, rb, map, count_ptr, max_rows, dst_rows);
+static hipError_t launch_copy(bool gather, const RowBuffers& bufs, const int32_t* map, const int32_t* count_ptr,
+                              int64_t max_rows, int64_t dst_rows, hipStream_t s) {
+  if (bufs.nbuf <= 0) return hipSuccess;
+  const dim3 grid(copy_grid(max_rows), (unsigned)bufs.nbuf), block(kCopyThreads);
+  if (gather)
+    hipLaunchKernelGGL((copy_rows_kernel<true>), grid, block, 0, s, bufs, map, count_ptr, max_rows, dst_rows);
   else
-    hipLaunchKernelGGL((copy_rows_kernel<false, false>), grid, block, 0, s, src, dst, rb, map, count_ptr, max_rows, dst_rows);
+    hipLaunchKernelGGL((copy_rows_kernel<false>), grid, block, 0, s, bufs, map, count_ptr, max_rows, dst_rows);
   return hipGetLastError();
 }
 
@@ -266,12 +267,7 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(rank_kernel, dim3((unsigned)(ntiles > 0 ? ntiles : 1)), dim3(kGatherThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  for (int b = 0; b < a.bufs.nbuf; ++b) {
-    e = launch_copy(true, a.bufs.vec16[b] != 0, a.bufs.src[b], a.bufs.dst[b], a.bufs.row_bytes[b], a.src_pos,
-                    a.cu_out + a.R, a.max_tokens, a.max_tokens, s);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  return launch_copy(true, a.bufs, a.src_pos, a.cu_out + a.R, a.max_tokens, a.max_tokens, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -281,9 +277,13 @@ hipError_t launch_scatter(const void* compacted, int64_t row_bytes, const int32_
                           const int32_t* count_ptr, int64_t max_tokens, void* full,
                           int64_t full_rows, hipStream_t s) {
   if (max_tokens <= 0) return hipSuccess;
-  const bool vec = (row_bytes % 16 == 0) && ((uintptr_t)compacted % 16 == 0) && ((uintptr_t)full % 16 == 0);
-  return launch_copy(false, vec, static_cast<const uint8_t*>(compacted), static_cast<uint8_t*>(full), row_bytes,
-                     index_map, count_ptr, max_tokens, full_rows, s);
+  RowBuffers one{};
+  one.nbuf = 1;
+  one.src[0] = static_cast<const uint8_t*>(compacted);
+  one.dst[0] = static_cast<uint8_t*>(full);
+  one.row_bytes[0] = row_bytes;
+  one.vec16[0] = (row_bytes % 16 == 0) && ((uintptr_t)compacted % 16 == 0) && ((uintptr_t)full % 16 == 0);
+  return launch_copy(false, one, index_map, count_ptr, max_tokens, full_rows, s);
 }
 
 }  // namespace up
