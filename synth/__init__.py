@@ -213,6 +213,8 @@ def random_scores(rng: np.random.Generator, nb: int, kind: str = "lognormal") ->
         x = np.where(rng.random(nb) < 0.05, rng.random(nb) * 100.0, rng.random(nb) * 1e-3)
     elif kind == "pareto":
         x = rng.pareto(1.0, size=nb)
+    elif kind == "constant":
+        x = np.full(nb, 0.25)
     else:
         raise ValueError(kind)
     return x.astype(np.float32)

@@ -124,6 +124,11 @@ def _scores_case(seed, lengths, G, kinds):
     (3, (65536,), 32, 128, 128, 0.98, ("lognormal",)),
     (4, (5000, 6000, 7000), 128, 0, 1, 1.0, ("sparse", "ties", "lognormal")),
     (5, tuple([300] * 16), 16, 16, 16, 0.5, ("ties", "lognormal", "pareto", "sparse")),
+    # more blocks than the kernel keeps in LDS (4096): keys re-read from the scores
+    (6, (300000, 5, 262208), 32, 16, 64, 0.95, ("lognormal", "ties", "ties")),
+    (7, (262208, 262144), 64, 128, 128, 0.99, ("pareto", "sparse")),
+    # all scores equal: the keys differ only in the block index
+    (8, (131072, 640, 64), 64, 128, 128, 0.99, ("constant",)),
 ])
 def test_topp_scores_in_bit_exact(seed, lengths, G, A, n, p, kinds):
     say(f"[topp] seed={seed} lengths={lengths[:5]} G={G} p={p}")

@@ -10,6 +10,11 @@
 // mass (over keys >= it) reaches thr = p * total; the kept blocks are exactly
 // the keys >= pivot.  Integer sums make the result independent of the order
 // of any reduction, so it matches a sequential sort-and-scan bit for bit.
+//
+// The digits start at the highest bit in which the request's keys differ
+// (the bits above it are common to all keys): block scores share their sign
+// and the top exponent bits, so a plain top-byte digit would put most keys
+// into a handful of bins, serialise their LDS atomics, and need one pass more.
 #include "common.h"
 
 namespace up {
@@ -45,7 +50,7 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
   __shared__ unsigned long long s_keys[kToppCache];
   __shared__ unsigned long long h_mass[256];
   __shared__ uint32_t h_cnt[256];
-  __shared__ unsigned long long red64[kToppWaves];
+  __shared__ unsigned long long red64[kToppWaves], red_or[kToppWaves], red_and[kToppWaves];
   __shared__ uint32_t red32[kToppWaves];
   __shared__ unsigned long long s_above, s_key;
   __shared__ int s_dsel;
@@ -61,16 +66,47 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
     return;
   }
   const float* sc = a.scores + b0;
-  if (a.scores_copy != nullptr && a.scores_copy != a.scores)
-    for (int g = tid; g < nb; g += kToppThreads) a.scores_copy[b0 + g] = sc[g];
+  const bool copy = a.scores_copy != nullptr && a.scores_copy != a.scores;
+  const bool cached = nb <= kToppCache;
+  auto key = [&](float x, int g) -> unsigned long long {
+    return ((unsigned long long)phi_bits(x) << 32) | (unsigned long long)(uint32_t)g;
+  };
 
-  // largest usable score -> binary exponent e, shift = 52 - ceil(log2 nb) - e
+  // one read of the scores: the largest usable one (for the mass scale), the
+  // keys (into LDS), and the OR / AND of all keys (for the first digit)
   uint32_t mxb = 0;
+  unsigned long long kor = 0ull, kand = ~0ull;
   for (int g = tid; g < nb; g += kToppThreads) {
-    const uint32_t b = __float_as_uint(sc[g]);
+    const float x = sc[g];
+    if (copy) a.scores_copy[b0 + g] = x;
+    const uint32_t b = __float_as_uint(x);
     if (usable(b) && b > mxb) mxb = b;
+    const unsigned long long k = key(x, g);
+    if (cached) s_keys[g] = k;
+    kor |= k;
+    kand &= k;
   }
-  mxb = block_reduce<uint32_t>(mxb, red32, true);
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t xm = __shfl_xor(mxb, o);
+    mxb = xm > mxb ? xm : mxb;
+    kor |= __shfl_xor(kor, o);
+    kand &= __shfl_xor(kand, o);
+  }
+  if (lane == 0) {
+    red32[wid] = mxb;
+    red_or[wid] = kor;
+    red_and[wid] = kand;
+  }
+  __syncthreads();   // (also publishes s_keys)
+  mxb = red32[0];
+  kor = red_or[0];
+  kand = red_and[0];
+  for (int w = 1; w < kToppWaves; ++w) {
+    mxb = red32[w] > mxb ? red32[w] : mxb;
+    kor |= red_or[w];
+    kand &= red_and[w];
+  }
+  // largest usable score -> binary exponent e, shift = 52 - ceil(log2 nb) - e
   int e = 0;
   if (mxb != 0u) (void)frexp((double)__uint_as_float(mxb), &e);
   const int nbits = (nb <= 1) ? 0 : 32 - __clz(nb - 1);
@@ -79,36 +115,31 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
   auto mass = [&](float x) -> unsigned long long {
     return usable(__float_as_uint(x)) ? (unsigned long long)ldexp((double)x, shift) : 0ull;
   };
-  auto key = [&](float x, int g) -> unsigned long long {
-    return ((unsigned long long)phi_bits(x) << 32) | (unsigned long long)(uint32_t)g;
-  };
   // the score back from the high half of a packed key (phi is invertible)
   auto score_of = [](unsigned long long k) -> float {
     const uint32_t ph = (uint32_t)(k >> 32);
     return __uint_as_float((ph & 0x80000000u) ? (ph ^ 0x80000000u) : ~ph);
   };
-  const bool cached = nb <= kToppCache;
   auto key_at = [&](int g) -> unsigned long long { return cached ? s_keys[g] : key(sc[g], g); };
 
   unsigned long long tot = 0;
-  for (int g = tid; g < nb; g += kToppThreads) {
-    const float x = sc[g];
-    if (cached) s_keys[g] = key(x, g);
-    tot += mass(x);
-  }
-  tot = block_reduce<unsigned long long>(tot, red64, false);   // (its barriers also publish s_keys)
+  for (int g = tid; g < nb; g += kToppThreads) tot += mass(score_of(key_at(g)));
+  tot = block_reduce<unsigned long long>(tot, red64, false);
   const double thr = a.p * (double)tot;
 
-  // weighted radix select, 8 bits per pass from the most significant digit
-  unsigned long long prefix = 0, above = 0, pivot = 0;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int sh = 56 - 8 * pass;
+  // weighted radix select, at most 8 bits per pass, from the highest bit in
+  // which keys differ down; `prefix` holds the bits of the pivot above `rem`
+  const unsigned long long diff = kor ^ kand;
+  int rem = diff ? 64 - __clzll((long long)diff) : 0;
+  unsigned long long prefix = rem >= 64 ? 0ull : kand >> rem, above = 0, pivot = kand;
+  while (rem > 0) {
+    const int sh = rem > 8 ? rem - 8 : 0, w = rem - sh;
     for (int d = tid; d < 256; d += kToppThreads) { h_mass[d] = 0ull; h_cnt[d] = 0u; }
     __syncthreads();
     for (int g = tid; g < nb; g += kToppThreads) {
       const unsigned long long k = key_at(g);
-      if (pass == 0 || (k >> (sh + 8)) == prefix) {
-        const int d = (int)((k >> sh) & 255ull);
+      if (rem >= 64 || (k >> rem) == prefix) {
+        const int d = (int)((k >> sh) & ((1ull << w) - 1ull));
         atomicAdd(&h_mass[d], mass(score_of(k)));
         atomicAdd(&h_cnt[d], 1u);
       }
@@ -151,20 +182,19 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
       }
     }
     __syncthreads();
-    prefix = (prefix << 8) | (unsigned long long)s_dsel;
+    prefix = (prefix << w) | (unsigned long long)s_dsel;
     above = s_above;
-    if (s_cnt == 1u || pass == 7) {
-      // the group holds a single key (or all 64 bits are fixed): find it
-      if (pass == 7) {
-        pivot = prefix;
-      } else {
-        for (int g = tid; g < nb; g += kToppThreads) {
-          const unsigned long long k = key_at(g);
-          if ((k >> sh) == prefix) s_key = k;
-        }
-        __syncthreads();
-        pivot = s_key;
+    rem = sh;
+    if (rem == 0) {
+      pivot = prefix;   // all 64 bits fixed
+    } else if (s_cnt == 1u) {
+      // the group holds a single key: find it
+      for (int g = tid; g < nb; g += kToppThreads) {
+        const unsigned long long k = key_at(g);
+        if ((k >> rem) == prefix) s_key = k;
       }
+      __syncthreads();
+      pivot = s_key;
       break;
     }
   }
