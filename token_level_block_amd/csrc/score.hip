@@ -16,7 +16,11 @@
 // range; the common case needs no per-logit max.  At each block end a lane
 // emits the log2-domain partial
 //     lse[g][row] = log2 sum_{i in block g} 2^(c z_i)
-// and folds it into a per-chunk partial.  The logits never reach memory.
+// and adds the block's linear sum (relative to the same reference, rescaled
+// with it) to a per-chunk sum.  Blocks are written in pairs: the first of two
+// is held in registers, and when the second closes one lane swap gives both
+// column sums (one block per half-wave), so a pair costs one logarithm and
+// one store.  The logits never reach memory.
 // Keys after a window row's own position are masked (causal masking), as
 // are keys past the end of the request.
 #include "common.h"
@@ -65,6 +69,13 @@ __device__ __forceinline__ float half_sum(float v) {
   return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
 }
 
+// half sums of two values at once: lanes 0-31 get a[l] + a[l + 32], lanes
+// 32-63 get b[l - 32] + b[l] (the swap trades a's upper half for b's lower)
+__device__ __forceinline__ float pair_sum(float a, float b) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+}
+
 // sum over this lane's 16 logits of 2^(c z + nrc), nrc = -c * ref
 __device__ __forceinline__ float tile_sum(const floatx16& acc, float cl2, float nrc) {
   float s0 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[0], cl2, nrc));
@@ -81,8 +92,9 @@ __device__ __forceinline__ float tile_sum(const floatx16& acc, float cl2, float 
   return (s0 + s1) + (s2 + s3);
 }
 
-// Largest tile partial accepted without rescaling; keeps every term of the
-// block sums far from fp32 overflow.
+// Largest tile partial accepted without rescaling; keeps the block and chunk
+// sums far from fp32 overflow (a lane adds at most 2^20 per 32-key tile, so
+// even a chunk of 2^20 keys stays below 2^35).
 constexpr float kRescaleAbove = 1048576.0f;   // 2^20
 
 // GT = G/32 tiles per block when G is 32, 64 or 128 (block ends known at
@@ -170,11 +182,15 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
 
   // ---- softmax state per query column ----
   const float cl2 = a.c;
-  float ref[C::NT], nrc[C::NT], eb[C::NT], cm[C::NT], ce[C::NT];
+  // ref: reference logit; eb: this lane's sum over the open block, ebh over
+  // the held block (number hold_gi, -1 if none) and cs over the chunk's
+  // closed blocks, all of 2^(c (z - ref))
+  float ref[C::NT], nrc[C::NT], eb[C::NT], ebh[C::NT], cs[C::NT];
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) {
-    ref[nt] = -INFINITY; nrc[nt] = INFINITY; eb[nt] = 0.f; cm[nt] = -INFINITY; ce[nt] = 0.f;
+    ref[nt] = -INFINITY; nrc[nt] = INFINITY; eb[nt] = 0.f; ebh[nt] = 0.f; cs[nt] = 0.f;
   }
+  int hold_gi = -1;
 
   // rare: raise the reference to the exact running maximum and redo the tile
   auto rescale = [&](floatx16 (&acc)[C::NT], float (&ts)[C::NT]) {
@@ -186,25 +202,38 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
       mx = fmaxf(mx, acc[nt][15]);
       const float mnew = fmaxf(ref[nt], half_max(mx));
       const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      eb[nt] *= __builtin_amdgcn_exp2f((ref[nt] - muse) * cl2);
+      const float f = __builtin_amdgcn_exp2f((ref[nt] - muse) * cl2);
+      eb[nt] *= f;
+      ebh[nt] *= f;
+      cs[nt] *= f;
       ref[nt] = mnew;
       nrc[nt] = -muse * cl2;
       ts[nt] = tile_sum(acc[nt], cl2, nrc[nt]);
     }
   };
-  // block gi is complete: emit its partial and fold it into the chunk partial
+  // block gi is complete: hold it, or emit it with the held one; either way
+  // add it to the chunk sum
   auto flush = [&](int gi) {
+    if (hold_gi < 0) {
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt) {
+        ebh[nt] = eb[nt];
+        cs[nt] += eb[nt];
+        eb[nt] = 0.f;
+      }
+      hold_gi = gi;
+      return;
+    }
+    const int64_t gl = gblk0 + (half ? gi : hold_gi);
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
-      const float E = half_sum(eb[nt]);
+      const float E = pair_sum(ebh[nt], eb[nt]);
       const float l = (ref[nt] == -INFINITY) ? -INFINITY : ref[nt] * cl2 + __log2f(E);
-      if (half == 0 && qrow[nt] >= 0) a.lse[(int64_t)(gblk0 + gi) * rows + qrow[nt]] = l;
-      const float cnew = fmaxf(cm[nt], l);
-      const float cuse = (cnew == -INFINITY) ? 0.f : cnew;
-      ce[nt] = ce[nt] * __builtin_amdgcn_exp2f(cm[nt] - cuse) + __builtin_amdgcn_exp2f(l - cuse);
-      cm[nt] = cnew;
+      if (qrow[nt] >= 0) a.lse[gl * rows + qrow[nt]] = l;
+      cs[nt] += eb[nt];
       eb[nt] = 0.f;
     }
+    hold_gi = -1;
   };
   // general tile: causal / tail masking, any block size
   auto process = [&](floatx16 (&acc)[C::NT], int kt) {
@@ -264,9 +293,10 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) eb[nt] += ts[nt];
         if constexpr (GT > 0 && GT <= C::SUB) {
-          if ((ks + 1) % GT == 0) flush((kb + ks * 32) / G);
+          if ((ks + 1) % GT == 0) flush((int)((unsigned)(kb + ks * 32) / (32u * GT)));
         } else if constexpr (GT > 0) {
-          if (ks + 1 == C::SUB && ((kb + C::KT) % G) == 0) flush((kb + ks * 32) / G);
+          if (ks + 1 == C::SUB && ((unsigned)(kb + C::KT) % (32u * GT)) == 0)
+            flush((int)((unsigned)(kb + ks * 32) / (32u * GT)));
         }
       }
     } else {
@@ -283,10 +313,20 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
     __syncthreads();
   }
 
+  if (hold_gi >= 0) {
+    // the chunk ended on the first of a pair
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      const float E = half_sum(ebh[nt]);
+      const float l = (ref[nt] == -INFINITY) ? -INFINITY : ref[nt] * cl2 + __log2f(E);
+      if (half == 0 && qrow[nt] >= 0) a.lse[(int64_t)(gblk0 + hold_gi) * rows + qrow[nt]] = l;
+    }
+  }
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) {
+    const float S = half_sum(cs[nt]);
     if (half == 0 && qrow[nt] >= 0) {
-      const float l = (cm[nt] == -INFINITY) ? -INFINITY : cm[nt] + __log2f(ce[nt]);
+      const float l = (ref[nt] == -INFINITY) ? -INFINITY : ref[nt] * cl2 + __log2f(S);
       a.chunk_lse[(int64_t)gc * rows + qrow[nt]] = l;
     }
   }
