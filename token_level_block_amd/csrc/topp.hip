@@ -48,11 +48,14 @@ __device__ __forceinline__ T block_reduce(T v, T* red, bool is_max) {
 
 __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
   __shared__ unsigned long long s_keys[kToppCache];
-  __shared__ unsigned long long h_mass[256];
-  __shared__ uint32_t h_cnt[256];
-  __shared__ unsigned long long red64[kToppWaves], red_or[kToppWaves], red_and[kToppWaves];
-  __shared__ uint32_t red32[kToppWaves];
-  __shared__ unsigned long long s_above, s_key;
+  // two histograms: one is filled while the other, used by the previous pass,
+  // is cleared, so a pass needs no barrier of its own for the clearing
+  __shared__ unsigned long long h_mass[2][256];
+  __shared__ uint32_t h_cnt[2][256];
+  __shared__ unsigned long long h_key[256];   // a key of each bin (the key, when the bin holds one)
+  __shared__ unsigned long long red64[kToppWaves];
+  __shared__ uint32_t red32[kToppWaves], red_or[kToppWaves], red_and[kToppWaves];
+  __shared__ unsigned long long s_above;
   __shared__ int s_dsel;
   __shared__ uint32_t s_cnt;
 
@@ -71,40 +74,41 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
   auto key = [&](float x, int g) -> unsigned long long {
     return ((unsigned long long)phi_bits(x) << 32) | (unsigned long long)(uint32_t)g;
   };
+  for (int d = tid; d < 256; d += kToppThreads) { h_mass[0][d] = 0ull; h_cnt[0][d] = 0u; }
 
   // one read of the scores: the largest usable one (for the mass scale), the
-  // keys (into LDS), and the OR / AND of all keys (for the first digit)
-  uint32_t mxb = 0;
-  unsigned long long kor = 0ull, kand = ~0ull;
+  // keys (into LDS), and the OR / AND of the keys' score halves (for the
+  // first digit)
+  uint32_t mxb = 0, por = 0u, pand = ~0u;
   for (int g = tid; g < nb; g += kToppThreads) {
     const float x = sc[g];
     if (copy) a.scores_copy[b0 + g] = x;
     const uint32_t b = __float_as_uint(x);
     if (usable(b) && b > mxb) mxb = b;
-    const unsigned long long k = key(x, g);
-    if (cached) s_keys[g] = k;
-    kor |= k;
-    kand &= k;
+    const uint32_t ph = phi_bits(x);
+    if (cached) s_keys[g] = ((unsigned long long)ph << 32) | (unsigned long long)(uint32_t)g;
+    por |= ph;
+    pand &= ph;
   }
   for (int o = 32; o >= 1; o >>= 1) {
     const uint32_t xm = __shfl_xor(mxb, o);
     mxb = xm > mxb ? xm : mxb;
-    kor |= __shfl_xor(kor, o);
-    kand &= __shfl_xor(kand, o);
+    por |= __shfl_xor(por, o);
+    pand &= __shfl_xor(pand, o);
   }
   if (lane == 0) {
     red32[wid] = mxb;
-    red_or[wid] = kor;
-    red_and[wid] = kand;
+    red_or[wid] = por;
+    red_and[wid] = pand;
   }
-  __syncthreads();   // (also publishes s_keys)
+  __syncthreads();   // (also publishes s_keys and the cleared first histogram)
   mxb = red32[0];
-  kor = red_or[0];
-  kand = red_and[0];
+  por = red_or[0];
+  pand = red_and[0];
   for (int w = 1; w < kToppWaves; ++w) {
     mxb = red32[w] > mxb ? red32[w] : mxb;
-    kor |= red_or[w];
-    kand &= red_and[w];
+    por |= red_or[w];
+    pand &= red_and[w];
   }
   // largest usable score -> binary exponent e, shift = 52 - ceil(log2 nb) - e
   int e = 0;
@@ -127,21 +131,31 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
   tot = block_reduce<unsigned long long>(tot, red64, false);
   const double thr = a.p * (double)tot;
 
-  // weighted radix select, at most 8 bits per pass, from the highest bit in
-  // which keys differ down; `prefix` holds the bits of the pivot above `rem`
-  const unsigned long long diff = kor ^ kand;
-  int rem = diff ? 64 - __clzll((long long)diff) : 0;
-  unsigned long long prefix = rem >= 64 ? 0ull : kand >> rem, above = 0, pivot = kand;
+  // Weighted radix select, at most 8 bits per pass, from the highest bit in
+  // which keys differ down; `prefix` holds the pivot's bits above `rem`.  The
+  // block indices 0 .. nb-1 fill the low half, so when all score halves agree
+  // the keys first differ in the top bit of nb - 1.
+  const uint32_t pdiff = por ^ pand;
+  int rem;
+  unsigned long long prefix;
+  if (pdiff != 0u) {
+    rem = 64 - __clz(pdiff);
+    prefix = rem >= 64 ? 0ull : (unsigned long long)(pand >> (rem - 32));
+  } else {
+    rem = nbits;
+    prefix = ((unsigned long long)pand << 32) >> rem;
+  }
+  unsigned long long above = 0, pivot = (unsigned long long)pand << 32;   // (the key, when nb == 1)
+  int buf = 0;
   while (rem > 0) {
     const int sh = rem > 8 ? rem - 8 : 0, w = rem - sh;
-    for (int d = tid; d < 256; d += kToppThreads) { h_mass[d] = 0ull; h_cnt[d] = 0u; }
-    __syncthreads();
     for (int g = tid; g < nb; g += kToppThreads) {
       const unsigned long long k = key_at(g);
       if (rem >= 64 || (k >> rem) == prefix) {
         const int d = (int)((k >> sh) & ((1ull << w) - 1ull));
-        atomicAdd(&h_mass[d], mass(score_of(k)));
-        atomicAdd(&h_cnt[d], 1u);
+        atomicAdd(&h_mass[buf][d], mass(score_of(k)));
+        atomicAdd(&h_cnt[buf][d], 1u);
+        h_key[d] = k;
       }
     }
     __syncthreads();
@@ -153,8 +167,8 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = 255 - 4 * lane - i;
-        m[i] = h_mass[d];
-        cn[i] = h_cnt[d];
+        m[i] = h_mass[buf][d];
+        cn[i] = h_cnt[buf][d];
         loc += m[i];
       }
       unsigned long long incl = loc;
@@ -180,29 +194,31 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
         s_above = abv;
         s_cnt = cfirst;
       }
+    } else {
+      // the other waves clear the histogram the next pass fills
+      for (int d = tid - kWave; d < 256; d += kToppThreads - kWave) {
+        h_mass[buf ^ 1][d] = 0ull;
+        h_cnt[buf ^ 1][d] = 0u;
+      }
     }
     __syncthreads();
-    prefix = (prefix << w) | (unsigned long long)s_dsel;
+    const int dsel = s_dsel;
+    prefix = (prefix << w) | (unsigned long long)dsel;
     above = s_above;
     rem = sh;
     if (rem == 0) {
       pivot = prefix;   // all 64 bits fixed
     } else if (s_cnt == 1u) {
-      // the group holds a single key: find it
-      for (int g = tid; g < nb; g += kToppThreads) {
-        const unsigned long long k = key_at(g);
-        if ((k >> rem) == prefix) s_key = k;
-      }
-      __syncthreads();
-      pivot = s_key;
+      pivot = h_key[dsel];   // the group holds a single key
       break;
     }
+    buf ^= 1;
   }
 
   // keep flags and the closed-form token count of the expanded mask
   const int A = a.A, n = a.n, G = a.G;
   const int w0 = max(max(N - n, 0), A);
-  unsigned long long cnt = 0;
+  uint32_t cnt = 0;
   for (int g = tid; g < nb; g += kToppThreads) {
     const bool kp = key_at(g) >= pivot;
     a.keep_block[b0 + g] = kp ? 1 : 0;
@@ -213,9 +229,9 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
     } else {
       c = max(0, min(hi, A) - lo) + max(0, hi - max(lo, w0));
     }
-    cnt += (unsigned long long)c;
+    cnt += (uint32_t)c;
   }
-  cnt = block_reduce<unsigned long long>(cnt, red64, false);
+  cnt = block_reduce<uint32_t>(cnt, red32, false);
   if (tid == 0) a.kept[r] = (int32_t)cnt;
 }
 
