@@ -5,6 +5,8 @@ import ctypes
 import math
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -248,3 +250,31 @@ def test_ffn_rejects_before_any_hip_work():
     assert lib.up_ffn_workspace_bytes(None, 10) == 0
     assert lib.up_ffn_forward(None, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == tlb.UP_ERR_NULL
     lib.up_ffn_destroy(None)
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/uniprefill.h compiles as C99 with -pedantic -Werror, and a C
+    program linked against the library sizes workspaces and gets the
+    documented status codes (tests/abi_check.c; host-side paths only)."""
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    exe = str(tmp_path / "abi_check")
+    libdir = os.path.dirname(tlb.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "abi_check.c"),
+                    "-L", libdir, "-luniprefill", f"-Wl,-rpath,{libdir}", "-o", exe],
+                   check=True, capture_output=True)
+    out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    got = dict(line.split(" ", 1) for line in out.splitlines())
+    assert got == {
+        "max_blocks": str(tlb.max_blocks(64, 1, 131072)),
+        "select_ws_positive": "1",
+        "compact_ws_positive": "1",
+        "status_ok": "set",
+        "select_null_params": str(tlb.UP_ERR_NULL),
+        "select_bad_p": str(tlb.UP_ERR_PARAM),
+        "select_small_workspace": str(tlb.UP_ERR_WORKSPACE),
+        "scatter_odd_rows": str(tlb.UP_ERR_PARAM),
+        "metadata_negative_layer": str(tlb.UP_ERR_SHAPE),
+    }
