@@ -278,6 +278,27 @@ def run_sweep(args, ev, stream):
     print(json.dumps({"sweep": records}), flush=True)
 
 
+def cpu_model():
+    """The host CPU's model name (first /proc/cpuinfo entry), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def blas_threads():
+    """Threads NumPy's BLAS may use: the OpenBLAS / OpenMP setting, else the core count."""
+    for var in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS"):
+        v = os.environ.get(var)
+        if v and v.isdigit():
+            return int(v)
+    return len(os.sched_getaffinity(0))
+
+
 def threads_used():
     n = len(os.sched_getaffinity(0))
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
@@ -519,7 +540,8 @@ def main():
         dt, _ = cpu_oracle_step(wl, cu, q, k, hidden_host)
         cpu = {"value": T / dt, "unit": "tokens/s", "cores": threads_used(), "kind": "oracle",
                "sample": f"one full step (select, compact, metadata, scatter-back) of the {T}-token request, "
-                         f"{dt:.1f} s wall"}
+                         f"{dt:.1f} s wall",
+               "cpu_model": cpu_model(), "blas_threads": blas_threads()}
         log(f"[bench] oracle step {dt:.2f} s -> {T / dt:.0f} tokens/s")
 
     line = {
