@@ -252,8 +252,15 @@ def run_sweep(args, ev, stream):
     configuration."""
     import torch
     import synth
-    wls = [synth.llama_4k(), synth.llama_varlen4(), synth.hybrid_64k("qwen_next", 64),
-           synth.hybrid_64k("gemma3", 64, p=0.98), synth.llama_128k(), synth.serving_16x128k()]
+    from dataclasses import replace
+    base = synth.llama_128k()
+    wls = [synth.llama_4k(), synth.llama_varlen4(),
+           *(synth.hybrid_64k("qwen_next", G) for G in (32, 64, 128)),
+           *(synth.hybrid_64k("gemma3", G, p=0.98) for G in (32, 64, 128)),
+           base,
+           # the window ablation of UniPrefill Table 4 at 128K: n = 32 and 512
+           *(replace(base, n=n, name=f"llama8b_128k_n{n}") for n in (32, 512)),
+           synth.serving_16x128k()]
     records = []
     for wl in wls:
         log(f"[sweep] {wl.name}: {wl.num_reqs} request(s), {sum(wl.lengths)} tokens")
@@ -262,7 +269,7 @@ def run_sweep(args, ev, stream):
         flops = sum(2.0 * min(wl.n, L) * wl.hq * wl.d * L for L in wl.lengths)
         rec = {"workload": wl.name, "requests": m["R"], "tokens": T, "kept": m["kept"],
                "num_heads_q": wl.hq, "num_heads_kv": wl.hkv, "head_dim": wl.d, "hidden": wl.hidden,
-               "G": wl.G, "p": wl.p, "ms_per_step": m["ms_per_step"],
+               "G": wl.G, "n": wl.n, "p": wl.p, "ms_per_step": m["ms_per_step"],
                "launch": "hip_graph" if m["ms_graph"] is not None else "eager",
                "tokens_per_s": T / (m["ms_per_step"] * 1e-3),
                "breakdown_ms": {"select": m["select_ms"], "score_kernel": m["score_ms"],

@@ -104,7 +104,11 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
   using C = ScoreCfg<D, NW, NT>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
 
-  const int gc = blockIdx.x;
+  // query slices of one key chunk are adjacent in dispatch order, so they run
+  // together and share the chunk's K through the caches
+  const int qslices = ((a.hq / a.hkv) * a.n + NW * C::QW - 1) / (NW * C::QW);
+  const int gc = (int)blockIdx.x / qslices;
+  const int zs = (int)blockIdx.x - gc * qslices;
   const int R = a.R;
   if (gc >= a.off.chunk[R]) return;
   const int r = find_owner(a.off.chunk, R, gc);
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
   const int gblk0 = a.off.blk[r];
 
   // ---- this lane's queries (one per 32-column tile) and their B fragments ----
-  const int qbase = (blockIdx.z * nwaves + wid) * C::QW;
+  const int qbase = (zs * nwaves + wid) * C::QW;
   int qrow[C::NT];      // output row h*n + t, or -1 if the lane's query is padding
   int qlim[C::NT];      // last visible key (request-relative), -1 if none
   bf16x8 qf[C::NT][C::KSTEPS];
@@ -335,12 +339,14 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
 template <int D, int GT>
 static hipError_t launch_score_dg(const ScoreArgs& a, hipStream_t s) {
   const ScoreLaunch L = score_launch_for(a.d, a.hq, a.hkv, a.n);
-  const dim3 grid((unsigned)a.max_chunks, (unsigned)a.hkv, (unsigned)L.zsplit);
-  if constexpr (D > 128) {
-    if (L.nt == 1) {
+  // x: key chunk x query slice (slices fastest), y: KV head
+  const dim3 grid((unsigned)(a.max_chunks * L.zsplit), (unsigned)a.hkv);
+  if (L.nt == 1) {
+    if (L.nw == 4)
+      hipLaunchKernelGGL((score_kernel<D, 4, GT, 1>), grid, dim3(4 * kWave), 0, s, a);
+    else
       hipLaunchKernelGGL((score_kernel<D, 8, GT, 1>), grid, dim3(8 * kWave), 0, s, a);
-      return hipGetLastError();
-    }
+    return hipGetLastError();
   }
   if (L.nw == 4)
     hipLaunchKernelGGL((score_kernel<D, 4, GT, 2>), grid, dim3(4 * kWave), 0, s, a);

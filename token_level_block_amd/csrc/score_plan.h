@@ -8,17 +8,20 @@ namespace up {
 
 // Launch shape of the score kernel for one KV head's qn = (Hq/Hkv)*n window
 // queries: waves per workgroup, 32-query column tiles per wave, query slices
-// (grid z), and how many such workgroups one CU holds at the kernel's
-// register use.  Two column tiles per wave halve the LDS reads per MFMA;
-// at d = 256 with at most 256 queries that would leave one wave per SIMD
-// (query fragments and accumulators of two tiles at d = 256 take 260
-// registers), so that case uses one tile per wave and eight waves.
+// (workgroups per key chunk), and how many such workgroups one CU holds at
+// the kernel's register use.  Two column tiles per wave halve the LDS reads
+// per MFMA; at d = 256 with at most 256 queries that would leave one wave per
+// SIMD (query fragments and accumulators of two tiles at d = 256 take 260
+// registers), so that case uses one tile per wave and eight waves.  At most
+// 128 queries (a short window, or few query heads per KV head) fill four
+// waves of one tile exactly, where two tiles would pad half the MFMA work.
 struct ScoreLaunch {
   int nw, nt, zsplit, per_cu;
 };
 
 inline ScoreLaunch score_launch_for(int32_t d, int32_t hq, int32_t hkv, int32_t n) {
   const int64_t qn = (int64_t)(hq / hkv) * n;
+  if (qn <= 128) return {4, 1, 1, 2};
   if (d > 128 && qn <= 256) return {8, 1, 1, 1};
   if (qn <= 256) return {4, 2, 1, 2};
   return {8, 2, (int)((qn + 511) / 512), 1};
