@@ -107,8 +107,11 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
   // query slices of one key chunk are adjacent in dispatch order, so they run
   // together and share the chunk's K through the caches
   const int qslices = ((a.hq / a.hkv) * a.n + NW * C::QW - 1) / (NW * C::QW);
-  const int gc = (int)blockIdx.x / qslices;
-  const int zs = (int)blockIdx.x - gc * qslices;
+  // workgroups are dealt to the 8 XCDs round-robin by id: ids 8 apart share
+  // an XCD (and its L2), so the slices of chunk c take ids 8 apart
+  const int lx = (int)blockIdx.x & 7, rest = (int)blockIdx.x >> 3;
+  const int zs = rest % qslices;
+  const int gc = (rest / qslices) * 8 + lx;
   const int R = a.R;
   if (gc >= a.off.chunk[R]) return;
   const int r = find_owner(a.off.chunk, R, gc);
@@ -340,7 +343,7 @@ template <int D, int GT>
 static hipError_t launch_score_dg(const ScoreArgs& a, hipStream_t s) {
   const ScoreLaunch L = score_launch_for(a.d, a.hq, a.hkv, a.n);
   // x: key chunk x query slice (slices fastest), y: KV head
-  const dim3 grid((unsigned)(a.max_chunks * L.zsplit), (unsigned)a.hkv);
+  const dim3 grid((unsigned)((a.max_chunks + 7) / 8 * 8 * L.zsplit), (unsigned)a.hkv);
   if (L.nt == 1) {
     if (L.nw == 4)
       hipLaunchKernelGGL((score_kernel<D, 4, GT, 1>), grid, dim3(4 * kWave), 0, s, a);

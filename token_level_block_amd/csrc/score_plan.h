@@ -33,14 +33,15 @@ inline ScoreLaunch score_launch_for(int32_t d, int32_t hq, int32_t hkv, int32_t 
 // per resident slot (256 CUs times the workgroups a CU holds).  The length is
 // a multiple of G (so no G-block straddles two workgroups), between the
 // multiple of G nearest 128 from above (one LDS stage: short batches still
-// fill the chip) and 8192 keys.
+// fill the chip) and 16384 keys (long batches then need fewer rounds of
+// workgroups).
 inline int32_t chunk_keys_for(int32_t G, int32_t d, int32_t hq, int32_t hkv, int32_t n, int64_t max_tokens) {
   const int32_t base = G >= 128 ? G : G * ((128 + G - 1) / G);
   if (hkv < 1 || hq < hkv || n < 1) return base;
   const ScoreLaunch L = score_launch_for(d, hq, hkv, n);
   const int64_t slots = 256 * (int64_t)L.per_cu;
   const int64_t want = (max_tokens * hkv * L.zsplit + slots - 1) / slots;
-  const int64_t cap = base > 8192 ? base : 8192;
+  const int64_t cap = base > 16384 ? base : 16384;
   int64_t ck = (want + base - 1) / base * base;
   if (ck < base) ck = base;
   if (ck > cap) ck = cap / base * base;
