@@ -29,11 +29,12 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def run_select(wl, cu, q, k, max_tokens=None):
+def run_select(wl, cu, q, k, max_tokens=None, scale=0.0, bufs=None):
     T = int(cu[-1])
     max_tokens = T if max_tokens is None else max_tokens
-    prm = tlb.make_params(wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p)
-    bufs = SelectBuffers.allocate(prm, wl.num_reqs, max_tokens)
+    if bufs is None:
+        prm = tlb.make_params(wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p, softmax_scale=scale)
+        bufs = SelectBuffers.allocate(prm, wl.num_reqs, max_tokens)
     bufs.keep_mask.fill_(0xAB)
     cu_d, qd, kd = upload_qk(wl, cu, q, k)
     bufs.run(qd, kd, cu_d)
@@ -74,7 +75,8 @@ TINY_CASES = [
     ((96, 128, 200), 2, 2, 64, 96, 0, 1, 1.0, "powerlaw"),
     ((4096,), 32, 8, 128, 64, 128, 128, 0.99, "hot"),
     ((70,) * 16, 4, 2, 64, 32, 8, 8, 0.9, "powerlaw"),
-    ((3000,), 4, 2, 128, 64, 128, 256, 0.99, "powerlaw"),    # query slice split over grid z
+    ((3000,), 4, 2, 128, 64, 128, 256, 0.99, "powerlaw"),    # 512 queries per KV head: one slice
+    ((3000, 700), 8, 2, 128, 64, 128, 256, 0.99, "powerlaw"),  # 1024 queries per KV head: two slices
 ]
 
 
@@ -94,6 +96,39 @@ def test_select_repeatable():
     for key in ("b", "keep", "mask", "kept"):
         assert np.array_equal(a[key], b[key]), key
     assert np.array_equal(a["b"].view(np.uint32), b["b"].view(np.uint32))
+
+
+def test_select_softmax_scale_override():
+    """The ABI's softmax_scale replaces 1/sqrt(d) inside the softmax (UniPrefill
+    Sec. 3.2 Eq. 2 prints 1/sqrt(d); the override serves other scalings)."""
+    wl = synth.tiny((1500, 333), hq=8, hkv=2, d=128, G=64, A=64, n=64, p=0.95, seed=21, kind="hot", hot=3,
+                    hot_lambda=6.0)
+    cu, q, k = synth.make_qk(wl)
+    for scale in (0.03, 0.25):
+        say(f"[scale] {scale}")
+        ref = oracle.select(q, k, cu, wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p, scale=scale)
+        got = run_select(wl, cu, q, k, scale=scale)
+        check_scores(got["b"], ref["b64"], ref["block_offsets"])
+        check_masks(ref, got["keep"], got["mask"], got["kept"], cu, wl)
+
+
+def test_select_reuses_buffers_for_a_smaller_batch():
+    """One set of buffers and workspace serves a long batch and then a shorter
+    one: the second call's results depend on nothing the first left behind."""
+    big = synth.tiny((4000, 2500), hq=8, hkv=2, d=128, G=64, A=64, n=64, p=0.99, seed=31, kind="powerlaw", c=1.5)
+    small = synth.tiny((700, 65), hq=8, hkv=2, d=128, G=64, A=64, n=64, p=0.99, seed=32, kind="hot", hot=2,
+                       hot_lambda=6.0)
+    cu_b, q_b, k_b = synth.make_qk(big)
+    cu_s, q_s, k_s = synth.make_qk(small)
+    prm = tlb.make_params(big.hq, big.hkv, big.d, big.G, big.A, big.n, big.p)
+    bufs = SelectBuffers.allocate(prm, 2, int(cu_b[-1]))
+    first = run_select(big, cu_b, q_b, k_b, bufs=bufs)
+    second = run_select(small, cu_s, q_s, k_s, bufs=bufs)
+    for wl, cu, q, k, got in ((big, cu_b, q_b, k_b, first), (small, cu_s, q_s, k_s, second)):
+        ref = oracle.select(q, k, cu, wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p)
+        assert np.array_equal(got["offs"], ref["block_offsets"])
+        check_scores(got["b"], ref["b64"], ref["block_offsets"])
+        check_masks(ref, got["keep"], got["mask"], got["kept"], cu, wl)
 
 
 def test_select_max_tokens_larger_than_stream():
