@@ -8,8 +8,9 @@
 // a double-buffered LDS ring with gfx950's direct global-to-LDS 16-byte loads
 // (no staging registers, XOR-swizzled rows so the A-operand reads are free of
 // bank conflicts) and feeds the A operand, so each 32x32 accumulator tile has
-// keys on rows and queries on columns and each lane owns one query column.  Each lane keeps, per query column, a reference logit
-// (the running maximum so far, raised only when needed) and sums 2^(c(z-ref))
+// keys on rows and queries on columns and each lane owns one query column.
+// Each lane keeps, per query column, a reference logit (the running maximum
+// so far, raised only when needed) and sums 2^(c(z-ref))
 // over the keys of the current G-block (c = softmax scale * log2 e).  A tile
 // whose per-lane partial sum exceeds 2^20 (or is not finite) is redone with
 // its exact maximum as the new reference, so every term stays within fp32
@@ -104,11 +105,11 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
   using C = ScoreCfg<D, NW, NT>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
 
-  // query slices of one key chunk are adjacent in dispatch order, so they run
-  // together and share the chunk's K through the caches
+  // Grid x enumerates (key chunk, query slice).  Workgroups are dealt to the
+  // 8 XCDs round-robin by id, so ids 8 apart share an XCD and its L2: the
+  // slices of one chunk take ids 8 apart and run together, reading the
+  // chunk's K from HBM once.
   const int qslices = ((a.hq / a.hkv) * a.n + NW * C::QW - 1) / (NW * C::QW);
-  // workgroups are dealt to the 8 XCDs round-robin by id: ids 8 apart share
-  // an XCD (and its L2), so the slices of chunk c take ids 8 apart
   const int lx = (int)blockIdx.x & 7, rest = (int)blockIdx.x >> 3;
   const int zs = rest % qslices;
   const int gc = (rest / qslices) * 8 + lx;
@@ -342,7 +343,8 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
 template <int D, int GT>
 static hipError_t launch_score_dg(const ScoreArgs& a, hipStream_t s) {
   const ScoreLaunch L = score_launch_for(a.d, a.hq, a.hkv, a.n);
-  // x: key chunk x query slice (slices fastest), y: KV head
+  // x: (key chunk, query slice) with the chunk count rounded up to 8 (ids
+  // past the last chunk exit at once), y: KV head
   const dim3 grid((unsigned)((a.max_chunks + 7) / 8 * 8 * L.zsplit), (unsigned)a.hkv);
   if (L.nt == 1) {
     if (L.nw == 4)
