@@ -278,3 +278,28 @@ def test_header_is_plain_c(tmp_path):
         "scatter_odd_rows": str(tlb.UP_ERR_PARAM),
         "metadata_negative_layer": str(tlb.UP_ERR_SHAPE),
     }
+
+
+def test_score_planner_invariants(tmp_path):
+    """score_plan.h (host C++): every window query covered by exactly the
+    planned slices, shapes within the kernel's register and wave budget,
+    chunk lengths multiples of G within their bounds, and the launch shapes
+    of the measured workloads (tests/plan_check.cc)."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no C++ compiler")
+    exe = str(tmp_path / "plan_check")
+    subprocess.run([gxx, "-std=c++17", "-O1", "-Wall", "-Wextra", "-Werror",
+                    os.path.join(ROOT, "tests", "plan_check.cc"), "-o", exe], check=True, capture_output=True)
+    p = subprocess.run([exe], capture_output=True, text=True)
+    assert p.returncode == 0, p.stderr
+    assert p.stdout.startswith("ok ") and int(p.stdout.split()[1]) > 1000
+
+
+def test_select_rejects_a_score_grid_beyond_32_bits():
+    """A window so long that (key chunks x query slices) would not fit the
+    grid's 32-bit x dimension is rejected at planning, not launched short."""
+    prm = p(num_heads_kv=1, window=1 << 19)          # Hq * n = 2^24, 32768 query slices
+    assert tlb.select_workspace_bytes(prm, 1, 2 ** 31 - 1) == 0
+    assert call_select(prm, T=2 ** 31 - 1) == tlb.UP_ERR_SHAPE
+    assert tlb.select_workspace_bytes(prm, 1, 4096) > 0   # the same parameters on a short batch plan fine

@@ -52,6 +52,12 @@ up_status plan_select(const up_select_params* prm, int32_t R, int64_t max_tokens
                                      max_tokens);
   L->max_blocks = max_tokens / G + R;
   L->max_chunks = max_tokens / L->chunk_keys + R;
+  if (L->scoring) {
+    // the score grid's x dimension enumerates (chunk rounded up to 8, query slice)
+    const up::ScoreLaunch SL = up::score_launch_for(prm->head_dim, prm->num_heads_q, prm->num_heads_kv,
+                                                    prm->window);
+    if ((L->max_chunks + 7) / 8 * 8 * (int64_t)SL.zsplit > INT32_MAX) return UP_ERR_SHAPE;
+  }
   const int64_t rows = (int64_t)prm->num_heads_q * prm->window;
   size_t off = 0;
   L->cu = off;      off = align_up(off + sizeof(int32_t) * (size_t)(R + 1));
