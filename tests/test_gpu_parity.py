@@ -77,6 +77,10 @@ TINY_CASES = [
     ((70,) * 16, 4, 2, 64, 32, 8, 8, 0.9, "powerlaw"),
     ((3000,), 4, 2, 128, 64, 128, 256, 0.99, "powerlaw"),    # 512 queries per KV head: one slice
     ((3000, 700), 8, 2, 128, 64, 128, 256, 0.99, "powerlaw"),  # 1024 queries per KV head: two slices
+    # 63 requests: the most whose offsets the score kernel derives itself (one per lane)
+    ((0,) + (33,) * 30 + (0,) + (70,) * 31, 4, 2, 64, 32, 8, 8, 0.9, "powerlaw"),
+    # 70 requests: offsets from the prep kernel
+    ((33,) * 40 + (0,) * 10 + (130,) * 20, 4, 2, 64, 32, 8, 8, 0.9, "powerlaw"),
 ]
 
 

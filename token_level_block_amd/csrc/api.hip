@@ -52,6 +52,7 @@ up_status plan_select(const up_select_params* prm, int32_t R, int64_t max_tokens
                                      max_tokens);
   L->max_blocks = max_tokens / G + R;
   L->max_chunks = max_tokens / L->chunk_keys + R;
+  if (L->max_chunks > INT32_MAX) return UP_ERR_SHAPE;   // one top-p workgroup per chunk
   if (L->scoring) {
     // the score grid's x dimension enumerates (chunk rounded up to 8, query slice)
     const up::ScoreLaunch SL = up::score_launch_for(prm->head_dim, prm->num_heads_q, prm->num_heads_kv,
@@ -135,7 +136,12 @@ up_status up_select_blocks(const up_select_params* prm, const void* q, int64_t q
   uint8_t* keep = keep_block ? keep_block : (ws + L.keep);
   const int32_t R = num_reqs;
 
-  if (up::launch_prep(cu_seqlens, R, max_tokens, prm->block_size, L.chunk_keys, off, block_offsets,
+  // a batch of at most 63 requests has its offsets derived inside the score
+  // kernel (one request per lane); otherwise, and without scoring, the prep
+  // kernel writes them first
+  const bool inline_offsets = L.scoring && R >= 1 && R <= up::kInlineOffsetsMaxReqs;
+  if (!inline_offsets &&
+      up::launch_prep(cu_seqlens, R, max_tokens, prm->block_size, L.chunk_keys, off, block_offsets,
                       stream) != hipSuccess)
     return UP_ERR_HIP;
 
@@ -162,6 +168,9 @@ up_status up_select_blocks(const up_select_params* prm, const void* q, int64_t q
     sa.lse = reinterpret_cast<float*>(ws + L.lse);
     sa.chunk_lse = reinterpret_cast<float*>(ws + L.chunk_lse);
     sa.max_chunks = L.max_chunks;
+    sa.cu_in = inline_offsets ? cu_seqlens : nullptr;
+    sa.cap = (int32_t)max_tokens;
+    sa.block_offsets_out = block_offsets;
     if (prm->prof_score_begin && hipEventRecord((hipEvent_t)prm->prof_score_begin, stream) != hipSuccess)
       return UP_ERR_HIP;
     if (up::launch_score(sa, stream) != hipSuccess) return UP_ERR_HIP;
@@ -198,6 +207,8 @@ up_status up_select_blocks(const up_select_params* prm, const void* q, int64_t q
   ta.kept = kept_per_req;
   ta.max_tokens = max_tokens;
   ta.max_blocks = L.max_blocks;
+  ta.chunk_keys = L.chunk_keys;
+  ta.max_chunks = L.max_chunks;
   if (up::launch_topp(ta, stream) != hipSuccess) return UP_ERR_HIP;
   return UP_OK;
 }

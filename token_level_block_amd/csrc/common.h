@@ -40,7 +40,14 @@ struct ScoreArgs {
   float* lse;            // [max_blocks][hq*n]  log2-domain block partials
   float* chunk_lse;      // [max_chunks][hq*n]  log2-domain chunk partials
   int64_t max_chunks;
+  // Offsets in the kernel itself (R < 64): cu_seqlens as the caller passed it,
+  // clamped to [0, cap]; `off` is then written by workgroup (0, 0), and
+  // block_offsets_out (optional) receives off.blk.  Null: `off` is ready.
+  const int32_t* cu_in;
+  int32_t cap;
+  int32_t* block_offsets_out;
 };
+constexpr int kInlineOffsetsMaxReqs = 63;
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
 
 struct CombineArgs {
@@ -65,6 +72,8 @@ struct ToppArgs {
   int32_t* kept;         // [R]
   int64_t max_tokens;
   int64_t max_blocks;
+  int32_t chunk_keys;    // tokens per key chunk (off.chunk counts these per request)
+  int64_t max_chunks;    // grid: one workgroup per chunk, ids past off.chunk[R] exit
 };
 hipError_t launch_topp(const ToppArgs& a, hipStream_t s);
 

@@ -114,11 +114,45 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
   const int zs = rest % qslices;
   const int gc = (rest / qslices) * 8 + lx;
   const int R = a.R;
-  if (gc >= a.off.chunk[R]) return;
-  const int r = find_owner(a.off.chunk, R, gc);
-  const int s = a.off.cu[r];
-  const int N = a.off.cu[r + 1] - s;
-  const int c = gc - a.off.chunk[r];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int r, s, N, c, gblk0;
+  if (a.cu_in != nullptr) {
+    // Offsets straight from cu_seqlens, request e on lane e (R < 64): the
+    // clamped running maximum, then prefix sums of the block and chunk counts.
+    // Every wave derives them itself; workgroup (0, 0) publishes them for the
+    // kernels that follow.
+    int32_t cu = lane <= R ? max(0, min(a.cu_in[lane], a.cap)) : 0;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t x = __shfl_up(cu, o);
+      if (lane >= o) cu = max(cu, x);
+    }
+    const int32_t len = (lane >= 1 && lane <= R) ? cu - __shfl_up(cu, 1) : 0;
+    int32_t nb = (len + a.G - 1) / a.G, nc = (len + a.chunk_keys - 1) / a.chunk_keys;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t xb = __shfl_up(nb, o), xc = __shfl_up(nc, o);
+      if (lane >= o) { nb += xb; nc += xc; }
+    }
+    if (blockIdx.x == 0 && blockIdx.y == 0 && wid == 0 && lane <= R) {
+      a.off.cu[lane] = cu;
+      a.off.blk[lane] = nb;
+      a.off.chunk[lane] = nc;
+      if (a.block_offsets_out) a.block_offsets_out[lane] = nb;
+    }
+    if (gc >= __shfl(nc, R)) return;
+    // owner: the last request whose first chunk is at or before gc
+    r = (int)__popcll(__ballot(lane < R && nc <= gc)) - 1;
+    s = __shfl(cu, r);
+    N = __shfl(cu, r + 1) - s;
+    c = gc - __shfl(nc, r);
+    gblk0 = __shfl(nb, r);
+  } else {
+    if (gc >= a.off.chunk[R]) return;
+    r = find_owner(a.off.chunk, R, gc);
+    s = a.off.cu[r];
+    N = a.off.cu[r + 1] - s;
+    c = gc - a.off.chunk[r];
+    gblk0 = a.off.blk[r];
+  }
   const int k0 = c * a.chunk_keys;
   const int k1 = min(N, k0 + a.chunk_keys);
   const int n = a.n;
@@ -129,9 +163,7 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
   const int rows = a.hq * n;
   const int qn = gq * n;                    // queries that read KV head j
   constexpr int nwaves = NW;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5;
-  const int gblk0 = a.off.blk[r];
 
   // ---- this lane's queries (one per 32-column tile) and their B fragments ----
   const int qbase = (zs * nwaves + wid) * C::QW;

@@ -15,6 +15,14 @@
 // (the bits above it are common to all keys): block scores share their sign
 // and the top exponent bits, so a plain top-byte digit would put most keys
 // into a handful of bins, serialise their LDS atomics, and need one pass more.
+//
+// The same kernel expands the kept blocks into the token mask.  One workgroup
+// runs per key chunk of a request (the chunks the score pass uses): every
+// workgroup of a request finds the same pivot (the selection is a pure
+// function of the request's scores), then writes the mask bytes of its own
+// chunk; the request's first chunk also writes the keep flags and the kept
+// count.  So the mask of a long request is written by many workgroups at once
+// without a second launch.
 #include "common.h"
 
 namespace up {
@@ -59,17 +67,22 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
   __shared__ int s_dsel;
   __shared__ uint32_t s_cnt;
 
-  const int r = blockIdx.x;
+  const int gc = blockIdx.x;
+  const int R = a.R;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // empty requests own no chunk: the first workgroup reports them
+  if (gc == 0)
+    for (int e = tid; e < R; e += kToppThreads)
+      if (a.off.cu[e + 1] == a.off.cu[e]) a.kept[e] = 0;
+  if (gc >= a.off.chunk[R]) return;
+  const int r = find_owner(a.off.chunk, R, gc);
+  const int c = gc - a.off.chunk[r];   // chunk within the request
+  const bool first = c == 0;           // writes the request's flags, count and score copy
   const int N = a.off.cu[r + 1] - a.off.cu[r];
   const int b0 = a.off.blk[r];
-  const int nb = a.off.blk[r + 1] - b0;
-  if (nb <= 0) {
-    if (tid == 0) a.kept[r] = 0;
-    return;
-  }
+  const int nb = a.off.blk[r + 1] - b0;   // >= 1: a request with a chunk has tokens
   const float* sc = a.scores + b0;
-  const bool copy = a.scores_copy != nullptr && a.scores_copy != a.scores;
+  const bool copy = first && a.scores_copy != nullptr && a.scores_copy != a.scores;
   const bool cached = nb <= kToppCache;
   auto key = [&](float x, int g) -> unsigned long long {
     return ((unsigned long long)phi_bits(x) << 32) | (unsigned long long)(uint32_t)g;
@@ -215,52 +228,40 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
     buf ^= 1;
   }
 
-  // keep flags and the closed-form token count of the expanded mask
   const int A = a.A, n = a.n, G = a.G;
-  const int w0 = max(max(N - n, 0), A);
-  uint32_t cnt = 0;
-  for (int g = tid; g < nb; g += kToppThreads) {
-    const bool kp = key_at(g) >= pivot;
-    a.keep_block[b0 + g] = kp ? 1 : 0;
-    const int lo = g * G, hi = min(N, lo + G);
-    int c;
-    if (kp) {
-      c = hi - lo;
-    } else {
-      c = max(0, min(hi, A) - lo) + max(0, hi - max(lo, w0));
+  if (first) {
+    // keep flags and the closed-form token count of the expanded mask
+    const int w0 = max(max(N - n, 0), A);
+    uint32_t cnt = 0;
+    for (int g = tid; g < nb; g += kToppThreads) {
+      const bool kp = key_at(g) >= pivot;
+      a.keep_block[b0 + g] = kp ? 1 : 0;
+      const int lo = g * G, hi = min(N, lo + G);
+      int t;
+      if (kp) {
+        t = hi - lo;
+      } else {
+        t = max(0, min(hi, A) - lo) + max(0, hi - max(lo, w0));
+      }
+      cnt += (uint32_t)t;
     }
-    cnt += (uint32_t)c;
+    cnt = block_reduce<uint32_t>(cnt, red32, false);
+    if (tid == 0) a.kept[r] = (int32_t)cnt;
   }
-  cnt = block_reduce<uint32_t>(cnt, red32, false);
-  if (tid == 0) a.kept[r] = (int32_t)cnt;
-}
 
-// token mask: M_i = keep[block(i)] or i < A or i >= N - n   (request-relative i)
-__global__ __launch_bounds__(256) void expand_kernel(Offsets off, int R, int G, int A, int n,
-                                                     const uint8_t* __restrict__ keep_block,
-                                                     uint8_t* __restrict__ mask, int64_t max_tokens) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= max_tokens) return;
-  const int T = off.cu[R];
-  if (i >= T || i < off.cu[0]) return;
-  const int r = find_owner(off.cu, R, i);
-  const int s = off.cu[r];
-  const int N = off.cu[r + 1] - s;
-  const int li = (int)(i - s);
-  const bool m = keep_block[off.blk[r] + li / G] != 0 || li < A || li >= N - n;
-  mask[i] = m ? 1 : 0;
+  // this chunk's token mask: M_i = keep[block(i)] or i < A or i >= N - n
+  // (request-relative i)
+  const int lo = c * a.chunk_keys, hi = min(N, lo + a.chunk_keys);
+  uint8_t* __restrict__ mrow = a.mask + a.off.cu[r];
+  for (int i = lo + tid; i < hi; i += kToppThreads) {
+    const bool m = i < A || i >= N - n || key_at(i / G) >= pivot;
+    mrow[i] = m ? 1 : 0;
+  }
 }
 
 hipError_t launch_topp(const ToppArgs& a, hipStream_t s) {
-  if (a.R > 0) {
-    hipLaunchKernelGGL(topp_kernel, dim3((unsigned)a.R), dim3(kToppThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (a.max_tokens > 0) {
-    hipLaunchKernelGGL(expand_kernel, dim3((unsigned)((a.max_tokens + 255) / 256)), dim3(256), 0, s,
-                       a.off, (int)a.R, (int)a.G, (int)a.A, (int)a.n, a.keep_block, a.mask, a.max_tokens);
-  }
+  if (a.max_chunks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topp_kernel, dim3((unsigned)a.max_chunks), dim3(kToppThreads), 0, s, a);
   return hipGetLastError();
 }
 
