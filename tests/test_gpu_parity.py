@@ -92,6 +92,29 @@ def test_select_small_shapes(idx):
     check_select(wl)
 
 
+@pytest.mark.parametrize("lengths", [(500, 0, 300), (33,) * 40 + (0,) * 10 + (130,) * 20],
+                         ids=["offsets_in_score_kernel", "offsets_from_prep"])
+def test_select_stream_with_leading_gap(lengths):
+    """Requests that start past token 0 (cu_seqlens[0] = 100): both ways of
+    forming the offsets (in the score kernel for a few requests, the prep
+    kernel for many) select from the right rows and leave the tokens before
+    the first request untouched."""
+    gap = 100
+    wl = synth.tiny(lengths, hq=4, hkv=2, d=64, G=32, A=8, n=8, p=0.9, seed=41, kind="powerlaw", c=1.5)
+    cu, q, k = synth.make_qk(wl)
+    rng = np.random.default_rng(42)
+    pad_q = rng.integers(-2 ** 15, 2 ** 15, size=(gap,) + q.shape[1:]).astype(np.int16).view(q.dtype)
+    pad_k = rng.integers(-2 ** 15, 2 ** 15, size=(gap,) + k.shape[1:]).astype(np.int16).view(k.dtype)
+    q2, k2 = np.concatenate([pad_q, q]), np.concatenate([pad_k, k])
+    cu2 = (cu + gap).astype(np.int32)
+    ref = oracle.select(q2, k2, cu2, wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p)
+    got = run_select(wl, cu2, q2, k2)
+    assert np.array_equal(got["offs"], ref["block_offsets"])
+    check_scores(got["b"], ref["b64"], ref["block_offsets"])
+    assert (got["mask"][:gap] == 0xAB).all()
+    check_masks(ref, got["keep"], got["mask"], got["kept"], cu2, wl)
+
+
 def test_select_repeatable():
     wl = synth.tiny((3000, 900), hq=8, hkv=2, d=128, G=64, A=128, n=128, p=0.99, seed=7, kind="powerlaw", c=1.4)
     cu, q, k = synth.make_qk(wl)
@@ -219,6 +242,9 @@ COMPACT_CASES = [
     (4, (300, 0), 0.0, (32,)),
     (5, (70000,), 1.0, (4,)),
     (6, (777, 0, 1234), 0.5, (36, 48, 100, 16)),   # wide unaligned rows, 3-unit rows, narrow aligned rows
+    # max_tokens = 131072 exactly: the largest stream ranked in one launch (case 2 takes the
+    # count + rank path, its max_tokens being 37 past 131072)
+    (7, (100000, 31035), 0.3, (8192, 4)),
 ]
 
 

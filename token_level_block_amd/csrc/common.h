@@ -145,6 +145,7 @@ struct KvWriteArgs {
 hipError_t launch_kv_write(const KvWriteArgs& a, bool vec, hipStream_t s);
 
 constexpr int kCountTile = 4096;    // tokens per compaction count workgroup
+constexpr int64_t kDirectRankMax = 131072;   // up to this many tokens compaction ranks in one launch
 constexpr int kGatherTile = 256;    // tokens per compaction gather workgroup
 
 // ---------------------------------------------------------------------------

@@ -143,6 +143,119 @@ __global__ __launch_bounds__(kGatherThreads) void rank_kernel(CompactArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Streams of at most kDirectRankMax tokens: one launch instead of count + rank.
+// Workgroup x ranks the tokens [4096 x, 4096 x + 4096) and finds the kept
+// tokens before its tile by reading the mask bytes before it (at most 128 KB:
+// one round of eight 16-byte loads per thread), so it needs no count pass.
+// ---------------------------------------------------------------------------
+constexpr int kDirectThreads = 1024;
+constexpr int kDirectTile = 4 * kDirectThreads;   // four tokens per thread
+
+__global__ __launch_bounds__(kDirectThreads) void rank_direct_kernel(CompactArgs a) {
+  __shared__ int32_t red[kDirectThreads / kWave];
+  __shared__ int32_t scan[kDirectThreads / kWave];   // the scans' own slots (red may still be read)
+  __shared__ int32_t excl[kDirectTile + 1];   // kept tokens of the tile before each position
+  __shared__ int32_t s_T, s_prefix, s_carry;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int32_t cap = (int32_t)(a.max_tokens < 0x7fffffff ? a.max_tokens : 0x7fffffff);
+  const int R = a.R;
+
+  int32_t m = 0;
+  for (int e = tid; e <= R; e += kDirectThreads) m = max(m, clamp_cu(a.cu_in[e], cap));
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o));
+  if (lane == 0) red[wid] = m;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t t = 0;
+    for (int w = 0; w < kDirectThreads / kWave; ++w) t = max(t, red[w]);
+    s_T = t;
+  }
+  __syncthreads();
+  const int32_t T = s_T;
+  const int64_t start = (int64_t)blockIdx.x * kDirectTile;
+  if (T == 0) {
+    if (blockIdx.x == 0)
+      for (int e = tid; e <= R; e += kDirectThreads) a.cu_out[e] = 0;
+    return;
+  }
+  if (start >= T) return;
+  const int64_t end = min<int64_t>(start + kDirectTile, T);
+
+  // kept tokens before the tile (start is a multiple of 16: whole pieces)
+  int c = 0;
+  {
+    constexpr int kUnroll = 8;
+    for (int64_t base = (int64_t)tid * 16; base < start; base += (int64_t)kDirectThreads * 16 * kUnroll) {
+      u32x4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t pos = base + (int64_t)u * kDirectThreads * 16;
+        v[u] = pos < start ? *reinterpret_cast<const u32x4*>(a.mask + pos) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        c += nonzero_bytes(v[u][0]) + nonzero_bytes(v[u][1]) + nonzero_bytes(v[u][2]) + nonzero_bytes(v[u][3]);
+    }
+  }
+  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+  if (lane == 0) red[wid] = c;
+  __syncthreads();
+  if (tid == 0) {
+    int t = 0;
+    for (int w = 0; w < kDirectThreads / kWave; ++w) t += red[w];
+    s_prefix = t;
+    s_carry = 0;
+  }
+  // (the barrier inside the scan below publishes s_prefix and s_carry)
+
+  // this thread's four tokens
+  const int64_t i0 = start + 4 * (int64_t)tid;
+  uint32_t kb = 0;   // bit j: token i0 + j is kept
+  if (i0 + 4 <= end) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(a.mask + i0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kb |= (((w >> (8 * j)) & 0xFFu) != 0u ? 1u : 0u) << j;
+  } else {
+    for (int j = 0; j < 4; ++j)
+      if (i0 + j < end && a.mask[i0 + j] != 0) kb |= 1u << j;
+  }
+  const int nk = __popc(kb);
+  const int incl = block_inclusive_scan<false>(nk, scan);
+  int run = incl - nk;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    excl[4 * tid + j] = run;
+    run += (kb >> j) & 1u;
+  }
+  if (tid == kDirectThreads - 1) excl[kDirectTile] = run;
+  __syncthreads();
+  const int32_t prefix = s_prefix;
+  {
+    int k = prefix + incl - nk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if ((kb >> j) & 1u) {
+        const int64_t i = i0 + j;
+        a.index_out[k] = a.index_in ? a.index_in[i] : (int32_t)i;
+        a.src_pos[k] = (int32_t)i;
+        ++k;
+      }
+    }
+  }
+  // new request offsets that fall inside this tile (the last tile also owns T)
+  for (int base = 0; base <= R; base += kDirectThreads) {
+    const int e = base + tid;
+    const int32_t v = (e <= R) ? clamp_cu(a.cu_in[e], cap) : 0;
+    const int32_t p = max(block_inclusive_scan<true>(v, scan), s_carry);
+    if (e <= R && p >= start && (p < end || (p == T && end == T))) a.cu_out[e] = prefix + excl[p - start];
+    __syncthreads();
+    if (tid == kDirectThreads - 1) s_carry = p;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Row copy over the kept rows k < count:  kGather: dst row k <- src row map[k]
 //                                         scatter: dst row map[k] <- src row k
 // 16-byte path: each wave takes contiguous runs of rows (an even number, the
@@ -264,6 +377,14 @@ static hipError_t launch_copy(bool gather, const RowBuffers& bufs, const int32_t
 }
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
+  if (a.max_tokens <= kDirectRankMax) {
+    const int64_t ntiles = (a.max_tokens + kDirectTile - 1) / kDirectTile;
+    hipLaunchKernelGGL(rank_direct_kernel, dim3((unsigned)(ntiles > 0 ? ntiles : 1)), dim3(kDirectThreads), 0, s,
+                       a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_copy(true, a.bufs, a.src_pos, a.cu_out + a.R, a.max_tokens, a.max_tokens, s);
+  }
   if (a.num_count_tiles > 0) {
     hipLaunchKernelGGL(count_kernel, dim3((unsigned)a.num_count_tiles), dim3(kCountThreads), 0, s,
                        a.mask, a.max_tokens, a.tile_count);

@@ -117,34 +117,46 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int r, s, N, c, gblk0;
   if (a.cu_in != nullptr) {
-    // Offsets straight from cu_seqlens, request e on lane e (R < 64): the
-    // clamped running maximum, then prefix sums of the block and chunk counts.
-    // Every wave derives them itself; workgroup (0, 0) publishes them for the
-    // kernels that follow.
-    int32_t cu = lane <= R ? max(0, min(a.cu_in[lane], a.cap)) : 0;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int32_t x = __shfl_up(cu, o);
-      if (lane >= o) cu = max(cu, x);
+    // Offsets straight from cu_seqlens (R < 64): lane e loads entry e; two
+    // uniform loops over the entries (lane reads into scalar registers) form
+    // the clamped running maximum and the prefix sums of the block and chunk
+    // counts, lane e keeping entry e of each.  Every wave derives them itself;
+    // workgroup (0, 0) publishes them for the kernels that follow.
+    const int32_t cuv = lane <= R ? max(0, min(a.cu_in[lane], a.cap)) : 0;
+    int32_t cu_l = 0, len_l = 0, run = 0;
+    for (int e = 0; e <= R; ++e) {
+      const int32_t v = max(run, __builtin_amdgcn_readlane(cuv, e));
+      if (lane == e) {
+        cu_l = v;
+        len_l = v - run;   // request e - 1 (lane 0: nothing before it)
+      }
+      run = v;
     }
-    const int32_t len = (lane >= 1 && lane <= R) ? cu - __shfl_up(cu, 1) : 0;
-    int32_t nb = (len + a.G - 1) / a.G, nc = (len + a.chunk_keys - 1) / a.chunk_keys;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int32_t xb = __shfl_up(nb, o), xc = __shfl_up(nc, o);
-      if (lane >= o) { nb += xb; nc += xc; }
+    if (lane == 0) len_l = 0;
+    const int32_t nb_l = (int32_t)((uint32_t)(len_l + a.G - 1) / (uint32_t)a.G);
+    const int32_t nc_l = (int32_t)((uint32_t)(len_l + a.chunk_keys - 1) / (uint32_t)a.chunk_keys);
+    int32_t blk_l = 0, chunk_l = 0, sb = 0, sc = 0;
+    for (int e = 0; e <= R; ++e) {
+      sb += __builtin_amdgcn_readlane(nb_l, e);
+      sc += __builtin_amdgcn_readlane(nc_l, e);
+      if (lane == e) {
+        blk_l = sb;
+        chunk_l = sc;
+      }
     }
     if (blockIdx.x == 0 && blockIdx.y == 0 && wid == 0 && lane <= R) {
-      a.off.cu[lane] = cu;
-      a.off.blk[lane] = nb;
-      a.off.chunk[lane] = nc;
-      if (a.block_offsets_out) a.block_offsets_out[lane] = nb;
+      a.off.cu[lane] = cu_l;
+      a.off.blk[lane] = blk_l;
+      a.off.chunk[lane] = chunk_l;
+      if (a.block_offsets_out) a.block_offsets_out[lane] = blk_l;
     }
-    if (gc >= __shfl(nc, R)) return;
+    if (gc >= sc) return;
     // owner: the last request whose first chunk is at or before gc
-    r = (int)__popcll(__ballot(lane < R && nc <= gc)) - 1;
-    s = __shfl(cu, r);
-    N = __shfl(cu, r + 1) - s;
-    c = gc - __shfl(nc, r);
-    gblk0 = __shfl(nb, r);
+    r = (int)__popcll(__ballot(lane < R && chunk_l <= gc)) - 1;
+    s = __builtin_amdgcn_readlane(cu_l, r);
+    N = __builtin_amdgcn_readlane(cu_l, r + 1) - s;
+    c = gc - __builtin_amdgcn_readlane(chunk_l, r);
+    gblk0 = __builtin_amdgcn_readlane(blk_l, r);
   } else {
     if (gc >= a.off.chunk[R]) return;
     r = find_owner(a.off.chunk, R, gc);
