@@ -296,6 +296,22 @@ def test_score_planner_invariants(tmp_path):
     assert p.stdout.startswith("ok ") and int(p.stdout.split()[1]) > 1000
 
 
+def test_copy_planner_invariants(tmp_path):
+    """copy_plan.h (host C++): the multiply-high division that maps a flat
+    copy's 16-byte units to rows equals integer division, every buffer of a
+    launch owns a non-empty workgroup range, and flat buffers fit 32-bit unit
+    indices and are covered by their workgroups (tests/copy_plan_check.cc)."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no C++ compiler")
+    exe = str(tmp_path / "copy_plan_check")
+    subprocess.run([gxx, "-std=c++17", "-O2", "-Wall", "-Wextra", "-Werror",
+                    os.path.join(ROOT, "tests", "copy_plan_check.cc"), "-o", exe], check=True, capture_output=True)
+    p = subprocess.run([exe], capture_output=True, text=True)
+    assert p.returncode == 0, p.stderr
+    assert p.stdout.startswith("ok ") and int(p.stdout.split()[1]) > 1000000
+
+
 def test_select_rejects_a_score_grid_beyond_32_bits():
     """A window so long that (key chunks x query slices) would not fit the
     grid's 32-bit x dimension is rejected at planning, not launched short."""

@@ -13,6 +13,9 @@
 //            rows back for the Eq. 8 scatter).
 // No atomics and no inter-workgroup waiting: every result is deterministic.
 #include "common.h"
+#include "copy_plan.h"
+
+static_assert(up::kMaxCompactBuffers == up::kMaxCopyBuffers, "one copy launch plans every compaction buffer");
 
 namespace up {
 
@@ -258,22 +261,18 @@ __global__ __launch_bounds__(kDirectThreads) void rank_direct_kernel(CompactArgs
 // ---------------------------------------------------------------------------
 // Row copy over the kept rows k < count:  kGather: dst row k <- src row map[k]
 //                                         scatter: dst row map[k] <- src row k
-// 16-byte path: each wave takes contiguous runs of rows (an even number, the
-// same for every busy wave: ceil(count / waves) rounded up to even, but at
-// most about 32 KiB of rows per run) and moves two rows per trip, up to
-// sixteen 16-byte nontemporal loads in flight per lane (the rows are streamed
-// once, so they bypass cache residency).  Equal runs keep the last trip from
-// running on a fraction of the waves; capping the run makes the waves take
-// their runs in rounds, so the rows in flight stay within a window of a few
-// hundred MB even when the buffers span tens of GB (one 32 KiB run per wave
-// per round moved 16 x 128K rows of 8 KiB 11 % faster than one long range per
-// wave).  4-byte path: rows of at most 32 bytes one per thread, wider rows one
-// per wave trip.
+// One launch moves every buffer; buffer b owns the workgroups
+// [plan.wg_begin[b], plan.wg_begin[b+1]) (copy_plan.h).
+// Flat buffers (16-byte rows wider than 32 bytes): the kept rows form one
+// stream of 16-byte units, unit i = (row i / units, piece i % units); a step
+// of the buffer's workgroups covers 256 consecutive units per workgroup and
+// consecutive workgroups take consecutive units, so the chip streams one
+// window of memory at a time (nontemporal: the rows are touched once).  This
+// ordering copied 8 KiB rows at ~6.1-6.3 TB/s against ~5.6 TB/s for waves that
+// each stream their own run of rows.  Narrow rows (<= 32 bytes): one row per
+// thread; other 4-byte-multiple rows: one row per wave.
 // ---------------------------------------------------------------------------
-constexpr int kCopyThreads = 256;
 constexpr int kCopyWaves = kCopyThreads / kWave;
-constexpr int64_t kNarrowRow = 32;   // rows up to this many bytes (not 16-byte aligned) go one per thread
-constexpr int64_t kCopyRunBytes = 32 << 10;   // longest run of rows a wave copies before the next round
 
 template <bool kGather>
 __device__ __forceinline__ void row_ends(const int32_t* __restrict__ map, int64_t k, int64_t& s, int64_t& d) {
@@ -281,98 +280,80 @@ __device__ __forceinline__ void row_ends(const int32_t* __restrict__ map, int64_
   d = kGather ? k : (int64_t)map[k];
 }
 
-// One launch moves every buffer: grid row y copies buffer y.  The path is
-// chosen per buffer (uniform over a workgroup): 16-byte rows wider than 32
-// bytes, narrow rows, or other 4-byte rows.
+// flat copy of `total` 16-byte units: a step of the nwg workgroups covers
+// nwg * 256 consecutive units, one per thread
 template <bool kGather>
-__global__ __launch_bounds__(kCopyThreads) void copy_rows_kernel(RowBuffers bufs,
+__device__ __forceinline__ void copy_flat(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                          const int32_t* __restrict__ map, uint32_t total, uint32_t units,
+                                          FastDiv div, int wg, int nwg, int64_t dst_rows) {
+  const u32x4* __restrict__ s16 = reinterpret_cast<const u32x4*>(src);
+  u32x4* __restrict__ d16 = reinterpret_cast<u32x4*>(dst);
+  // 64-bit position: a 32-bit one could wrap past total near 2^32 and never end
+  const uint64_t step = (uint64_t)nwg * kCopyThreads;
+  for (uint64_t i = (uint64_t)wg * kCopyThreads + threadIdx.x; i < total; i += step) {
+    const uint32_t k = fastdiv((uint32_t)i, div);
+    const uint32_t j = (uint32_t)i - k * units;
+    int64_t sr, dr;
+    row_ends<kGather>(map, k, sr, dr);
+    if (dr < 0 || dr >= dst_rows) continue;
+    const u32x4 v = __builtin_nontemporal_load(s16 + sr * units + j);
+    __builtin_nontemporal_store(v, d16 + dr * units + j);
+  }
+}
+
+template <bool kGather>
+__global__ __launch_bounds__(kCopyThreads) void copy_rows_kernel(RowBuffers bufs, CopyPlan plan,
                                                                  const int32_t* __restrict__ map,
                                                                  const int32_t* __restrict__ count_ptr,
                                                                  int64_t max_rows, int64_t dst_rows) {
-  const int b = blockIdx.y;
+  int b = 0;
+  while (b + 1 < bufs.nbuf && (int)blockIdx.x >= plan.wg_begin[b + 1]) ++b;
+  const int wg = (int)blockIdx.x - plan.wg_begin[b];
+  const int nwg = plan.wg_begin[b + 1] - plan.wg_begin[b];
   const uint8_t* __restrict__ src = bufs.src[b];
   uint8_t* __restrict__ dst = bufs.dst[b];
   const int64_t rb = bufs.row_bytes[b];
-  const int lane = threadIdx.x & 63;
-  const int64_t gw = (int64_t)blockIdx.x * kCopyWaves + (threadIdx.x >> 6);
-  const int64_t W = (int64_t)gridDim.x * kCopyWaves;
   const int64_t count = min<int64_t>(*count_ptr, max_rows);
-  if (bufs.vec16[b] != 0 && rb > kNarrowRow) {
-    const int64_t per = (((count + W - 1) / W) + 1) & ~(int64_t)1;
-    const int64_t run = min<int64_t>(per, max<int64_t>(2, (kCopyRunBytes / rb) & ~(int64_t)1));
-    const int units = (int)(rb >> 4);
-    for (int64_t k0 = gw * run; k0 < count; k0 += W * run)
-    for (int64_t k = k0, k1 = min<int64_t>(count, k0 + run); k < k1; k += 2) {
-      int64_t s[2], d[2];
-      bool ok[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        ok[j] = k + j < k1;
-        if (ok[j]) row_ends<kGather>(map, k + j, s[j], d[j]);
-        ok[j] = ok[j] && d[j] >= 0 && d[j] < dst_rows;
-      }
-      for (int u0 = 0; u0 < units; u0 += 8 * kWave) {
-        u32x4 v[2][8];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const u32x4* sp = reinterpret_cast<const u32x4*>(src + (ok[j] ? s[j] : 0) * rb);
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int u = u0 + lane + x * kWave;
-            if (ok[j] && u < units) v[j][x] = __builtin_nontemporal_load(sp + u);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          u32x4* dp = reinterpret_cast<u32x4*>(dst + (ok[j] ? d[j] : 0) * rb);
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int u = u0 + lane + x * kWave;
-            if (ok[j] && u < units) __builtin_nontemporal_store(v[j][x], dp + u);
-          }
-        }
-      }
-    }
-  } else if (rb <= kNarrowRow) {
+  if (plan.flat[b]) {
+    const uint32_t total = (uint32_t)count * plan.units[b];   // < 2^32: checked when planned
+    copy_flat<kGather>(src, dst, map, total, plan.units[b], plan.div[b], wg, nwg, dst_rows);
+  } else if (rb <= kCopyNarrowRow) {
     // narrow rows (positions, indices): one thread per row
-    const int64_t t = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x;
-    const int64_t T = (int64_t)gridDim.x * kCopyThreads;
     const int units = (int)(rb >> 2);
-    for (int64_t k = t; k < count; k += T) {
-      int64_t s, d;
-      row_ends<kGather>(map, k, s, d);
-      if (d < 0 || d >= dst_rows) continue;
-      const uint32_t* sp = reinterpret_cast<const uint32_t*>(src + s * rb);
-      uint32_t* dp = reinterpret_cast<uint32_t*>(dst + d * rb);
+    for (int64_t k = (int64_t)wg * kCopyThreads + threadIdx.x; k < count; k += (int64_t)nwg * kCopyThreads) {
+      int64_t sr, dr;
+      row_ends<kGather>(map, k, sr, dr);
+      if (dr < 0 || dr >= dst_rows) continue;
+      const uint32_t* sp = reinterpret_cast<const uint32_t*>(src + sr * rb);
+      uint32_t* dp = reinterpret_cast<uint32_t*>(dst + dr * rb);
       for (int u = 0; u < units; ++u) dp[u] = sp[u];
     }
   } else {
-    for (int64_t k = gw; k < count; k += W) {
-      int64_t s, d;
-      row_ends<kGather>(map, k, s, d);
-      if (d < 0 || d >= dst_rows) continue;
-      const uint32_t* sp = reinterpret_cast<const uint32_t*>(src + s * rb);
-      uint32_t* dp = reinterpret_cast<uint32_t*>(dst + d * rb);
-      const int units = (int)(rb >> 2);
+    // other rows of 4-byte multiples: one row per wave
+    const int lane = threadIdx.x & 63;
+    const int units = (int)(rb >> 2);
+    for (int64_t k = (int64_t)wg * kCopyWaves + (threadIdx.x >> 6); k < count; k += (int64_t)nwg * kCopyWaves) {
+      int64_t sr, dr;
+      row_ends<kGather>(map, k, sr, dr);
+      if (dr < 0 || dr >= dst_rows) continue;
+      const uint32_t* sp = reinterpret_cast<const uint32_t*>(src + sr * rb);
+      uint32_t* dp = reinterpret_cast<uint32_t*>(dst + dr * rb);
       for (int u = lane; u < units; u += kWave) dp[u] = sp[u];
     }
   }
 }
 
-static unsigned copy_grid(int64_t max_rows) {
-  // up to 256 CUs x 64 waves, fewer for small batches
-  const int64_t want = (max_rows + kCopyWaves - 1) / kCopyWaves;
-  return (unsigned)(want < 1 ? 1 : (want > 4096 ? 4096 : want));
-}
-
 static hipError_t launch_copy(bool gather, const RowBuffers& bufs, const int32_t* map, const int32_t* count_ptr,
                               int64_t max_rows, int64_t dst_rows, hipStream_t s) {
-  if (bufs.nbuf <= 0) return hipSuccess;
-  const dim3 grid(copy_grid(max_rows), (unsigned)bufs.nbuf), block(kCopyThreads);
+  if (bufs.nbuf <= 0 || max_rows <= 0) return hipSuccess;
+  CopyPlan plan;
+  if (!make_copy_plan(bufs.nbuf, bufs.row_bytes, bufs.vec16, max_rows, &plan)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)plan.wg_begin[bufs.nbuf]), block(kCopyThreads);
   if (gather)
-    hipLaunchKernelGGL((copy_rows_kernel<true>), grid, block, 0, s, bufs, map, count_ptr, max_rows, dst_rows);
+    hipLaunchKernelGGL((copy_rows_kernel<true>), grid, block, 0, s, bufs, plan, map, count_ptr, max_rows, dst_rows);
   else
-    hipLaunchKernelGGL((copy_rows_kernel<false>), grid, block, 0, s, bufs, map, count_ptr, max_rows, dst_rows);
+    hipLaunchKernelGGL((copy_rows_kernel<false>), grid, block, 0, s, bufs, plan, map, count_ptr, max_rows,
+                       dst_rows);
   return hipGetLastError();
 }
 
