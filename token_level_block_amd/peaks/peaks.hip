@@ -9,9 +9,11 @@
 //                    values in [0.5, 2) with random signs are used.  Two
 //                    independent accumulator chains per wave, two waves per
 //                    SIMD (the score kernel's occupancy).
-//   upk_copy_launch  a streaming device copy, one 8 KiB piece per wave at a
-//                    time with eight 16-byte nontemporal loads in flight per
-//                    lane (the row copies' access pattern without the gather).
+//   upk_copy_launch  a streaming device copy: one 16-byte nontemporal unit
+//                    per thread, consecutive workgroups on consecutive units
+//                    (the row copies' access pattern without the gather), by
+//                    default one unit per thread in a single pass, the fastest
+//                    plain copy shape measured on the part.
 //
 // Built into libuppeaks.so, separate from libuniprefill.so; only the
 // benchmark loads it.
@@ -72,24 +74,12 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_peak_kernel(float* out) {
   out[t] = s;
 }
 
-// each wave copies whole 8 KiB pieces: lane l moves 16-byte units l + 64 x,
-// x = 0..7, all eight loads in flight before the stores
+// thread t of workgroup w copies units w*256 + t + k*(grid*256), k = 0, 1, ...
 __global__ __launch_bounds__(kCopyThreads) void copy_peak_kernel(const u32x4* __restrict__ src,
                                                                  u32x4* __restrict__ dst, int64_t n) {
-  constexpr int kUnits = 8 * 64;   // 16-byte units per 8 KiB piece
-  const int lane = threadIdx.x & 63;
-  const int64_t waves = (int64_t)gridDim.x * (kCopyThreads / 64);
-  const int64_t pieces = (n + kUnits - 1) / kUnits;
-  for (int64_t c = (int64_t)blockIdx.x * (kCopyThreads / 64) + (threadIdx.x >> 6); c < pieces; c += waves) {
-    const int64_t base = c * kUnits + lane;
-    u32x4 v[8];
-#pragma unroll
-    for (int x = 0; x < 8; ++x)
-      if (base + 64 * x < n) v[x] = __builtin_nontemporal_load(src + base + 64 * x);
-#pragma unroll
-    for (int x = 0; x < 8; ++x)
-      if (base + 64 * x < n) __builtin_nontemporal_store(v[x], dst + base + 64 * x);
-  }
+  const int64_t step = (int64_t)gridDim.x * kCopyThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x; i < n; i += step)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 }  // namespace
@@ -114,12 +104,17 @@ int32_t upk_mfma_launch(float* out, int32_t blocks, hipStream_t stream) {
 }
 
 // Enqueue a copy of `bytes` (a multiple of 16; both pointers 16-byte aligned)
-// from src to dst on `stream`.  Returns 0, -1 on bad arguments, or the HIP error.
+// from src to dst on `stream` with `blocks` workgroups of 256 threads, or with
+// one thread per 16-byte unit when blocks < 1 (at most 2^31 - 1 workgroups).
+// Returns 0, -1 on bad arguments, or the HIP error.
 int32_t upk_copy_launch(const void* src, void* dst, int64_t bytes, int32_t blocks, hipStream_t stream) {
-  if (src == nullptr || dst == nullptr || bytes <= 0 || bytes % 16 != 0 || blocks < 1) return -1;
+  if (src == nullptr || dst == nullptr || bytes <= 0 || bytes % 16 != 0) return -1;
   if (((uintptr_t)src | (uintptr_t)dst) % 16 != 0) return -1;
-  hipLaunchKernelGGL(copy_peak_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, stream,
-                     (const u32x4*)src, (u32x4*)dst, bytes / 16);
+  const int64_t n = bytes / 16;
+  const int64_t g = blocks >= 1 ? blocks : (n + kCopyThreads - 1) / kCopyThreads;
+  if (g > 0x7fffffff) return -1;
+  hipLaunchKernelGGL(copy_peak_kernel, dim3((unsigned)g), dim3(kCopyThreads), 0, stream,
+                     (const u32x4*)src, (u32x4*)dst, n);
   return (int32_t)hipGetLastError();
 }
 
