@@ -315,10 +315,12 @@ def threads_used():
     return n
 
 
-def measure_step(wl, steps, warmup, ev, stream):
+def measure_step(wl, steps, warmup, ev, stream, pipelined=False):
     """Set up one workload (seeded inputs resident in HBM) and time the step:
     eager, eager with per-phase events (breakdown), and replayed from a HIP
-    graph after three bit-exact checks against the eager step."""
+    graph after three bit-exact checks against the eager step.  With
+    `pipelined`, also two independent batches in flight on two streams (see
+    measure_two_in_flight)."""
     import numpy as np
     import torch
     import synth
@@ -402,6 +404,14 @@ def measure_step(wl, steps, warmup, ev, stream):
         step(stream, marks[i])
     torch.cuda.synchronize()
 
+    # two batches in flight on two streams; before any graph capture, since in
+    # a process that has captured and replayed a HIP graph the two streams were
+    # measured to run one after the other (0.46 against 0.36 ms per batch)
+    two = None
+    if pipelined:
+        two = measure_two_in_flight(args.steps, ev, stream, ref_out, kept_now, R, T, prm, cu_d, qd, kd, hidden, pos,
+                                    mb_lengths=np.diff(cu), first=(sel, cb, mb, out, pos_out, full))
+
     # ... and the same step captured once in a HIP graph and replayed K times
     # (every call only enqueues kernels, so the whole step is capturable); each
     # of three checked replays must reproduce the eager step's outputs bit for bit
@@ -443,10 +453,79 @@ def measure_step(wl, steps, warmup, ev, stream):
     scatter_ms = mean("t3", "t4")
 
     kept = int(sel.kept[:R].sum().item())
+    if two is not None:
+        two["ms_one_stream"] = ms_per_step
+        two["speedup"] = ms_per_step / two["ms_per_batch"]
     return dict(wl=wl, T=T, R=R, kept=kept, cu=cu, q=q, k=k, cu_d=cu_d, sel=sel, cb=cb, nwords=nwords,
                 ms_eager=ms_eager, ms_graph=ms_graph, graph_note=graph_note, ms_per_step=ms_per_step,
                 score_ms=score_ms, select_ms=select_ms, compact_ms=compact_ms, meta_ms=meta_ms,
-                scatter_ms=scatter_ms, release=lambda: None)
+                scatter_ms=scatter_ms, two=two, release=lambda: None)
+
+
+def measure_two_in_flight(steps, ev, stream, ref_out, kept_now, R, T, prm, cu_d, qd, kd, hidden, pos,
+                          mb_lengths, first):
+    """Throughput with two independent batches of the same workload in flight,
+    each with its own buffers and stream (default priority).  The score GEMM is
+    bound by the matrix core and VALU and reads 0.27 GB, the row copies by HBM
+    (1.7 GB), so each batch's selection waits for the other's: the score
+    kernels alternate and each one runs beside the other batch's copies.
+    Eager launches (the GPU stays busy well past the launch cost).  Both
+    batches' outputs must equal the single-stream step's bit for bit."""
+    import torch
+    from token_level_block_amd.runner import CompactBuffers, MetadataBuffers, SelectBuffers, run_scatter_back
+
+    sel2 = SelectBuffers.allocate(prm, R, T)
+    cb2 = CompactBuffers.allocate(R, T)
+    mb2 = MetadataBuffers.allocate(mb_lengths, num_layers=32, max_drops=4)
+    out2, pos_out2 = torch.empty_like(first[3]), torch.empty_like(first[4])
+    full2 = hidden.clone()
+    sets = [first, (sel2, cb2, mb2, out2, pos_out2, full2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    done = [torch.cuda.Event(), torch.cuda.Event()]   # each batch's selection finished
+
+    def rounds(n):
+        cur = torch.cuda.current_stream()
+        for st in streams:
+            st.wait_stream(cur)
+        for i in range(n):
+            for b in (0, 1):
+                sel, cb, mb, out, pos_out, full = sets[b]
+                st = streams[b]
+                if i > 0 or b == 1:
+                    st.wait_event(done[1 - b])   # the other batch's selection
+                h = st.cuda_stream
+                sel.run(qd, kd, cu_d, stream=h)
+                done[b].record(st)
+                cb.run(sel.keep_mask, cu_d, [hidden, pos], [out, pos_out], stream=h)
+                mb.run(0, cu_d, cb.cu_out, stream=h)
+                run_scatter_back(out, cb.index_out, cb.cu_out, R, T, full, stream=h)
+        for st in streams:
+            cur.wait_stream(st)
+
+    prm.prof_score_begin = prm.prof_score_end = None
+    # new streams run slowly for their first few milliseconds of work (measured:
+    # the first 20 rounds at 0.57-0.62 ms per batch, later ones at 0.36-0.39)
+    rounds(max(steps, 20))
+    torch.cuda.synchronize()
+    start, stop = ev.new(), ev.new()
+    ev.record(start, stream)
+    rounds(steps)
+    ev.record(stop, stream)
+    ms = ev.ms(start, stop) / (2 * steps)
+    torch.cuda.synchronize()
+    same = True
+    for sel, cb, mb, out, pos_out, full in sets:
+        got = (sel.keep_mask[:T], sel.kept[:R], cb.cu_out, cb.index_out[:kept_now], out[:kept_now],
+               pos_out[:kept_now], full)
+        same = same and all(torch.equal(a, b) for a, b in zip(got, ref_out))
+    del sel2, cb2, mb2, out2, pos_out2, full2
+    torch.cuda.empty_cache()
+    if not same:
+        raise RuntimeError("a batch run beside another differs from the single-stream step")
+    return {"batches_in_flight": 2, "streams": 2, "ms_per_batch": ms, "tokens_per_s": T / (ms * 1e-3),
+            "outputs_bit_exact": True, "launch": "eager",
+            "schedule": "each batch's selection waits for the other's, so each score GEMM runs beside "
+                        "the other batch's row copies"}
 
 
 def main():
@@ -495,7 +574,7 @@ def main():
         run_sweep(args, ev, stream)
         return
     wl = synth.llama_128k()
-    m = measure_step(wl, args.steps, args.warmup, ev, stream)
+    m = measure_step(wl, args.steps, args.warmup, ev, stream, pipelined=not args.step_only)
     T, R, kept, cu, q, k, cu_d, sel, cb, nwords = (m[x] for x in ("T", "R", "kept", "cu", "q", "k", "cu_d", "sel",
                                                                     "cb", "nwords"))
     ms_eager, ms_graph, graph_note, ms_per_step = m["ms_eager"], m["ms_graph"], m["graph_note"], m["ms_per_step"]
@@ -603,6 +682,8 @@ def main():
         "breakdown_ms": {"select": select_ms, "score_kernel": score_ms, "compact": compact_ms,
                          "metadata": meta_ms, "scatter_back": scatter_ms},
         "select_compact_tokens_per_s": sel_compact_tps,
+        # the same workload with two batches in flight (not `value`: that is one batch at a time)
+        "two_batches_in_flight": m["two"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
