@@ -539,6 +539,9 @@ def main():
                          "and the measured peaks (for short profiled runs)")
     ap.add_argument("--sweep", action="store_true",
                     help="time the step on every workload shape (4K to 16 x 128K) instead of the benchmark line")
+    ap.add_argument("--two-in-flight", action="store_true",
+                    help="also time two independent batches in flight on two streams (two_batches_in_flight); "
+                         "off by default so that a kernel trace of the default run holds only serial launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -574,7 +577,7 @@ def main():
         run_sweep(args, ev, stream)
         return
     wl = synth.llama_128k()
-    m = measure_step(wl, args.steps, args.warmup, ev, stream, pipelined=not args.step_only)
+    m = measure_step(wl, args.steps, args.warmup, ev, stream, pipelined=args.two_in_flight)
     T, R, kept, cu, q, k, cu_d, sel, cb, nwords = (m[x] for x in ("T", "R", "kept", "cu", "q", "k", "cu_d", "sel",
                                                                     "cb", "nwords"))
     ms_eager, ms_graph, graph_note, ms_per_step = m["ms_eager"], m["ms_graph"], m["graph_note"], m["ms_per_step"]
@@ -682,7 +685,8 @@ def main():
         "breakdown_ms": {"select": select_ms, "score_kernel": score_ms, "compact": compact_ms,
                          "metadata": meta_ms, "scatter_back": scatter_ms},
         "select_compact_tokens_per_s": sel_compact_tps,
-        # the same workload with two batches in flight (not `value`: that is one batch at a time)
+        # with --two-in-flight: the same workload with two batches in flight (not `value`:
+        # that is one batch at a time)
         "two_batches_in_flight": m["two"],
         "cpu_baseline": cpu,
     }
