@@ -115,6 +115,39 @@ def test_select_stream_with_leading_gap(lengths):
     check_masks(ref, got["keep"], got["mask"], got["kept"], cu2, wl)
 
 
+def random_case(seed):
+    """A seeded random small workload: 1 to 70 requests (some empty, lengths
+    ragged around and between the sink, window and block sizes), any head
+    dimension, GQA ratio, block size, sink count, window and p."""
+    rng = np.random.default_rng(1000 + seed)
+    d = int(rng.choice([64, 128, 256]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([32, 64, 96, 128]))
+    n = int(rng.choice([1, 8, 32, 64, 100, 128]))
+    A = int(rng.choice([0, 4, 64, 128]))
+    p = float(rng.choice([0.5, 0.9, 0.95, 0.98, 0.99, 1.0]))
+    R = int(rng.choice([1, 2, 3, 5, 16, 40, 63, 64, 70]))
+    budget = 24000 // max(1, hq * n // 64)          # keep the oracle's work to a second or two
+    lengths = []
+    for _ in range(R):
+        u = rng.random()
+        L = 0 if u < 0.08 else int(rng.integers(1, 2 * G + n + A + 2)) if u < 0.4 else int(rng.integers(1, 4000))
+        lengths.append(L)
+    while sum(lengths) > budget and max(lengths) > 1:
+        i = int(np.argmax(lengths))
+        lengths[i] //= 2
+    kind = str(rng.choice(["hot", "powerlaw"]))
+    return synth.tiny(tuple(lengths), hq=hq, hkv=hkv, d=d, G=G, A=A, n=n, p=p, seed=2000 + seed, kind=kind,
+                      hot=int(rng.integers(1, 6)), hot_lambda=float(rng.uniform(3.0, 8.0)),
+                      c=float(rng.uniform(0.8, 1.8)))
+
+
+@pytest.mark.parametrize("seed", range(20), ids=[f"r{i}" for i in range(20)])
+def test_select_random_shapes(seed):
+    check_select(random_case(seed), label=f"random {seed}")
+
+
 def test_select_repeatable():
     wl = synth.tiny((3000, 900), hq=8, hkv=2, d=128, G=64, A=128, n=128, p=0.99, seed=7, kind="powerlaw", c=1.4)
     cu, q, k = synth.make_qk(wl)
@@ -288,6 +321,60 @@ def test_compact_and_scatter_bit_exact(seed, lengths, rho, row_bytes):
                                  cb.index_out, cb.cu_out, R, max_tokens, full)
                 torch.cuda.synchronize()
                 assert np.array_equal(full.cpu().numpy().view(np.uint32), want)
+
+
+@pytest.mark.parametrize("seed", range(12), ids=[f"r{i}" for i in range(12)])
+def test_compact_and_scatter_random(seed):
+    """Seeded random compactions: 1 to 70 requests (some empty), keep ratios
+    from 0 to 1 (block-structured or per token), one to four buffers with rows
+    of 4 bytes to 8 KiB (16-byte multiples and not), max_tokens at or past the
+    stream (around the one-launch rank limit too), with and without an index
+    map; bit-exact against the oracle, then the Eq. 8 scatter back."""
+    rng = np.random.default_rng(3000 + seed)
+    R = int(rng.choice([1, 2, 5, 16, 63, 70]))
+    big = seed % 4 == 0
+    lengths = [0 if rng.random() < 0.1 else int(rng.integers(1, (131072 // R) if big else 3000)) for _ in range(R)]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    max_tokens = T + int(rng.choice([0, 1, 37, 4096]))
+    rho = float(rng.choice([0.0, 0.05, 0.4, 0.9, 1.0]))
+    if rng.random() < 0.5:
+        blk = (rng.random(T // 64 + 1) < rho).astype(np.uint8)
+        m = blk[np.arange(T) // 64]
+    else:
+        m = (rng.random(T) < rho).astype(np.uint8)
+    mask = np.zeros(max_tokens, np.uint8)
+    mask[:T] = m * rng.integers(1, 256, T).astype(np.uint8)
+    mask[T:] = 1
+    nbuf = int(rng.integers(1, 5))
+    row_bytes = tuple(int(rng.choice([4, 8, 12, 16, 32, 36, 48, 64, 100, 2048, 7680, 8192])) for _ in range(nbuf))
+    if big:
+        row_bytes = tuple(min(rb, 2048) for rb in row_bytes)   # keep the host copies small
+    say(f"[compact-rand] seed={seed} R={R} T={T} max_tokens={max_tokens} rho={rho} rows={row_bytes}")
+    bufs_h = [rng.integers(0, 2 ** 32, size=(max_tokens, rb // 4), dtype=np.uint64).astype(np.uint32)
+              for rb in row_bytes]
+    use_index = bool(rng.random() < 0.5)
+    index_in = rng.permutation(4 * max_tokens + 1)[:max_tokens].astype(np.int32) if use_index else None
+    outs, idx, cu_out = oracle.compact(mask, cu, bufs_h, index_in)
+    src = [dev(b.view(np.int32)) for b in bufs_h]
+    dst = [torch.full_like(t, -7) for t in src]
+    cb = CompactBuffers.allocate(R, max_tokens)
+    cb.run(dev(mask), dev(cu), src, dst, index_in=dev(index_in) if use_index else None)
+    torch.cuda.synchronize()
+    K = len(idx)
+    assert np.array_equal(cb.cu_out[: R + 1].cpu().numpy(), cu_out)
+    assert np.array_equal(cb.index_out[:K].cpu().numpy(), idx)
+    for o, d in zip(outs, dst):
+        assert np.array_equal(d[:K].cpu().numpy().view(np.uint32), o)
+        assert (d[K:].cpu().numpy() == -7).all()
+    if not use_index and K:
+        b = int(rng.integers(0, nbuf))
+        proc = (outs[b].astype(np.uint64) + 1).astype(np.uint32)
+        want = oracle.scatter_back(bufs_h[b], proc, idx, K)
+        full = dev(bufs_h[b].view(np.int32))
+        run_scatter_back(dev(proc.view(np.int32)), cb.index_out, cb.cu_out, R, max_tokens, full)
+        torch.cuda.synchronize()
+        assert np.array_equal(full.cpu().numpy().view(np.uint32), want)
 
 
 def test_compact_twice_composes_index():
