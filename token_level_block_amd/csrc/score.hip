@@ -49,6 +49,8 @@ struct ScoreCfg {
   static_assert(STAGE % (1024 * NW) == 0, "a stage must split evenly into 1 KB wave loads");
 };
 
+template <int V> struct IntC { static constexpr int value = V; };
+
 // s_waitcnt vmcnt(0) with the other counters left free (gfx9 encoding)
 constexpr int kWaitVmcnt0 = 0x0F70;
 
@@ -100,8 +102,11 @@ constexpr float kRescaleAbove = 1048576.0f;   // 2^20
 
 // GT = G/32 tiles per block when G is 32, 64 or 128 (block ends known at
 // compile time in the plain stages), 0 for any other multiple of 32.
+// Launch bounds: eight-wave workgroups run one per CU, four-wave ones two per
+// CU (the residency the chunk planner counts on); either way two waves per
+// SIMD, so each wave may use 256 registers.
 template <int D, int NW, int GT, int NT>
-__global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void score_kernel(ScoreArgs a) {
   using C = ScoreCfg<D, NW, NT>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
 
@@ -243,6 +248,11 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
     ref[nt] = -INFINITY; nrc[nt] = INFINITY; eb[nt] = 0.f; ebh[nt] = 0.f; cs[nt] = 0.f;
   }
   int hold_gi = -1;
+  // byte offset of a lane's entry in a block pair's partials: half 0 writes the
+  // held block, half 1 the next one (row qrow of each)
+  uint32_t pair_off[C::NT];
+#pragma unroll
+  for (int nt = 0; nt < C::NT; ++nt) pair_off[nt] = (uint32_t)(qrow[nt] + half * rows) * 4u;
 
   // rare: raise the reference to the exact running maximum and redo the tile
   auto rescale = [&](floatx16 (&acc)[C::NT], float (&ts)[C::NT]) {
@@ -276,12 +286,14 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
       hold_gi = gi;
       return;
     }
-    const int64_t gl = gblk0 + (half ? gi : hold_gi);
+    // blocks close in order, so the pair is (gi - 1, gi): the held block's row
+    // base is uniform and each lane adds its own fixed byte offset
+    char* pb = reinterpret_cast<char*>(a.lse + (int64_t)(gblk0 + hold_gi) * rows);
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
       const float E = pair_sum(ebh[nt], eb[nt]);
       const float l = (ref[nt] == -INFINITY) ? -INFINITY : ref[nt] * cl2 + __log2f(E);
-      if (qrow[nt] >= 0) a.lse[gl * rows + qrow[nt]] = l;
+      if (qrow[nt] >= 0) *reinterpret_cast<float*>(pb + pair_off[nt]) = l;
       cs[nt] += eb[nt];
       eb[nt] = 0.f;
     }
@@ -319,11 +331,14 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
   __syncthreads();
 
   floatx16 acc[C::NT];
-  for (int st = 0; st < nstages; ++st) {
+  // one stage; the LDS buffer it reads is a compile-time constant, so the
+  // fragment addresses are loop-invariant registers plus immediate offsets
+  auto stage = [&](int st, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     const int kb = k0 + st * C::KT;
     // the next stage lands in the other buffer while this one is consumed
-    if (st + 1 < nstages) load_stage(kb + C::KT, (st + 1) & 1);
-    const uint8_t* sbuf = smem + (st & 1) * C::STAGE;
+    if (st + 1 < nstages) load_stage(kb + C::KT, BUF ^ 1);
+    const uint8_t* sbuf = smem + BUF * C::STAGE;
     const bool plain = (kb + C::KT <= k1) && (kb + C::KT <= N - ne);
     if (GT > 0 && plain) {
       // every tile full and unmasked; block ends at fixed tiles
@@ -363,7 +378,13 @@ __global__ __launch_bounds__(NW * 64, 1) void score_kernel(ScoreArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's loads of the next stage have landed
     __syncthreads();
+  };
+  int st = 0;
+  for (; st + 1 < nstages; st += 2) {
+    stage(st, IntC<0>{});
+    stage(st + 1, IntC<1>{});
   }
+  if (st < nstages) stage(st, IntC<0>{});
 
   if (hold_gi >= 0) {
     // the chunk ended on the first of a pair
@@ -397,10 +418,16 @@ static hipError_t launch_score_dg(const ScoreArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((score_kernel<D, 8, GT, 1>), grid, dim3(8 * kWave), 0, s, a);
     return hipGetLastError();
   }
-  if (L.nw == 4)
-    hipLaunchKernelGGL((score_kernel<D, 4, GT, 2>), grid, dim3(4 * kWave), 0, s, a);
-  else
+  if (L.nw == 4) {
+    // four waves of two tiles only at d <= 128 (score_launch_for): at d = 256 the
+    // fragments would not fit the two workgroups per CU its launch bounds promise
+    if constexpr (D <= 128)
+      hipLaunchKernelGGL((score_kernel<D, 4, GT, 2>), grid, dim3(4 * kWave), 0, s, a);
+    else
+      return hipErrorInvalidValue;
+  } else {
     hipLaunchKernelGGL((score_kernel<D, 8, GT, 2>), grid, dim3(8 * kWave), 0, s, a);
+  }
   return hipGetLastError();
 }
 
