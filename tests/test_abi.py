@@ -280,6 +280,18 @@ def test_header_is_plain_c(tmp_path):
     }
 
 
+def build_host_check(gxx, name, tmp_path):
+    """Build a host-side planner check with g++, under AddressSanitizer and
+    UndefinedBehaviorSanitizer (any finding aborts the run) where the toolchain
+    has their runtimes, else plainly."""
+    exe = str(tmp_path / name.replace(".cc", ""))
+    base = [gxx, "-std=c++17", "-O1", "-g", "-Wall", "-Wextra", "-Werror", os.path.join(ROOT, "tests", name), "-o", exe]
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+    if subprocess.run(base[:1] + san + base[1:], capture_output=True).returncode != 0:
+        subprocess.run(base, check=True, capture_output=True)
+    return exe
+
+
 def test_score_planner_invariants(tmp_path):
     """score_plan.h (host C++): every window query covered by exactly the
     planned slices, shapes within the kernel's register and wave budget,
@@ -288,9 +300,7 @@ def test_score_planner_invariants(tmp_path):
     gxx = shutil.which("g++")
     if gxx is None:
         pytest.skip("no C++ compiler")
-    exe = str(tmp_path / "plan_check")
-    subprocess.run([gxx, "-std=c++17", "-O1", "-Wall", "-Wextra", "-Werror",
-                    os.path.join(ROOT, "tests", "plan_check.cc"), "-o", exe], check=True, capture_output=True)
+    exe = build_host_check(gxx, "plan_check.cc", tmp_path)
     p = subprocess.run([exe], capture_output=True, text=True)
     assert p.returncode == 0, p.stderr
     assert p.stdout.startswith("ok ") and int(p.stdout.split()[1]) > 1000
@@ -304,9 +314,7 @@ def test_copy_planner_invariants(tmp_path):
     gxx = shutil.which("g++")
     if gxx is None:
         pytest.skip("no C++ compiler")
-    exe = str(tmp_path / "copy_plan_check")
-    subprocess.run([gxx, "-std=c++17", "-O2", "-Wall", "-Wextra", "-Werror",
-                    os.path.join(ROOT, "tests", "copy_plan_check.cc"), "-o", exe], check=True, capture_output=True)
+    exe = build_host_check(gxx, "copy_plan_check.cc", tmp_path)
     p = subprocess.run([exe], capture_output=True, text=True)
     assert p.returncode == 0, p.stderr
     assert p.stdout.startswith("ok ") and int(p.stdout.split()[1]) > 1000000
