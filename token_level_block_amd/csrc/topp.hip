@@ -27,7 +27,7 @@
 
 namespace up {
 
-constexpr int kToppThreads = 512;
+constexpr int kToppThreads = 1024;
 constexpr int kToppWaves = kToppThreads / kWave;
 constexpr int kToppCache = 4096;   // requests with at most this many blocks keep their keys in LDS
 
@@ -61,7 +61,6 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
   __shared__ unsigned long long h_mass[2][256];
   __shared__ uint32_t h_cnt[2][256];
   __shared__ unsigned long long h_key[256];   // a key of each bin (the key, when the bin holds one)
-  __shared__ unsigned long long red64[kToppWaves];
   __shared__ uint32_t red32[kToppWaves], red_or[kToppWaves], red_and[kToppWaves];
   __shared__ unsigned long long s_above;
   __shared__ int s_dsel;
@@ -139,10 +138,9 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
   };
   auto key_at = [&](int g) -> unsigned long long { return cached ? s_keys[g] : key(sc[g], g); };
 
-  unsigned long long tot = 0;
-  for (int g = tid; g < nb; g += kToppThreads) tot += mass(score_of(key_at(g)));
-  tot = block_reduce<unsigned long long>(tot, red64, false);
-  const double thr = a.p * (double)tot;
+  // thr = p * (total integer mass); only wave 0 uses it, and it takes the total
+  // from the first pass's histogram, which every key enters
+  double thr = 0.0;
 
   // Weighted radix select, at most 8 bits per pass, from the highest bit in
   // which keys differ down; `prefix` holds the pivot's bits above `rem`.  The
@@ -160,6 +158,7 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
   }
   unsigned long long above = 0, pivot = (unsigned long long)pand << 32;   // (the key, when nb == 1)
   int buf = 0;
+  bool first_pass = true;
   while (rem > 0) {
     const int sh = rem > 8 ? rem - 8 : 0, w = rem - sh;
     for (int g = tid; g < nb; g += kToppThreads) {
@@ -189,6 +188,7 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
         const unsigned long long x = __shfl_up(incl, o);
         if (lane >= o) incl += x;
       }
+      if (first_pass) thr = a.p * (double)__shfl(incl, 63);   // all 256 bins: the total mass
       unsigned long long run = above + (incl - loc);
       int first = -1;
       unsigned long long abv = 0;
@@ -226,6 +226,7 @@ __global__ __launch_bounds__(kToppThreads) void topp_kernel(ToppArgs a) {
       break;
     }
     buf ^= 1;
+    first_pass = false;
   }
 
   const int A = a.A, n = a.n, G = a.G;
