@@ -278,6 +278,10 @@ COMPACT_CASES = [
     # max_tokens = 131072 exactly: the largest stream ranked in one launch (case 2 takes the
     # count + rank path, its max_tokens being 37 past 131072)
     (7, (100000, 31035), 0.3, (8192, 4)),
+    # more requests than the one-launch rank kernel's threads (the stream length and
+    # the new offsets are then formed by the whole workgroup), below and above 131072 tokens
+    (8, (3, 0, 17) * 500, 0.5, (16, 4)),
+    (9, (100,) * 1400, 0.3, (32,)),
 ]
 
 

@@ -155,27 +155,29 @@ constexpr int kDirectThreads = 1024;
 constexpr int kDirectTile = 4 * kDirectThreads;   // four tokens per thread
 
 __global__ __launch_bounds__(kDirectThreads) void rank_direct_kernel(CompactArgs a) {
-  __shared__ int32_t red[kDirectThreads / kWave];
-  __shared__ int32_t scan[kDirectThreads / kWave];   // the scans' own slots (red may still be read)
+  __shared__ int32_t red_c[kDirectThreads / kWave], red_k[kDirectThreads / kWave];
+  __shared__ int32_t scan[kDirectThreads / kWave];
   __shared__ int32_t excl[kDirectTile + 1];   // kept tokens of the tile before each position
-  __shared__ int32_t s_T, s_prefix, s_carry;
+  __shared__ int32_t s_carry;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int32_t cap = (int32_t)(a.max_tokens < 0x7fffffff ? a.max_tokens : 0x7fffffff);
   const int R = a.R;
 
-  int32_t m = 0;
-  for (int e = tid; e <= R; e += kDirectThreads) m = max(m, clamp_cu(a.cu_in[e], cap));
-  for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o));
-  if (lane == 0) red[wid] = m;
-  __syncthreads();
-  if (tid == 0) {
-    int32_t t = 0;
-    for (int w = 0; w < kDirectThreads / kWave; ++w) t = max(t, red[w]);
-    s_T = t;
+  // stream length T = the largest clamped offset: every wave finds it itself
+  // for fewer than 1024 requests, else the workgroup shares the reads
+  int32_t T = 0;
+  if (R < kDirectThreads) {
+    for (int e = lane; e <= R; e += kWave) T = max(T, clamp_cu(a.cu_in[e], cap));
+    for (int o = 32; o >= 1; o >>= 1) T = max(T, __shfl_xor(T, o));
+  } else {
+    for (int e = tid; e <= R; e += kDirectThreads) T = max(T, clamp_cu(a.cu_in[e], cap));
+    for (int o = 32; o >= 1; o >>= 1) T = max(T, __shfl_xor(T, o));
+    if (lane == 0) scan[wid] = T;
+    __syncthreads();
+    for (int w = 0; w < kDirectThreads / kWave; ++w) T = max(T, scan[w]);
+    __syncthreads();   // scan is reused below
   }
-  __syncthreads();
-  const int32_t T = s_T;
   const int64_t start = (int64_t)blockIdx.x * kDirectTile;
   if (T == 0) {
     if (blockIdx.x == 0)
@@ -201,16 +203,6 @@ __global__ __launch_bounds__(kDirectThreads) void rank_direct_kernel(CompactArgs
         c += nonzero_bytes(v[u][0]) + nonzero_bytes(v[u][1]) + nonzero_bytes(v[u][2]) + nonzero_bytes(v[u][3]);
     }
   }
-  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
-  if (lane == 0) red[wid] = c;
-  __syncthreads();
-  if (tid == 0) {
-    int t = 0;
-    for (int w = 0; w < kDirectThreads / kWave; ++w) t += red[w];
-    s_prefix = t;
-    s_carry = 0;
-  }
-  // (the barrier inside the scan below publishes s_prefix and s_carry)
 
   // this thread's four tokens
   const int64_t i0 = start + 4 * (int64_t)tid;
@@ -224,29 +216,57 @@ __global__ __launch_bounds__(kDirectThreads) void rank_direct_kernel(CompactArgs
       if (i0 + j < end && a.mask[i0 + j] != 0) kb |= 1u << j;
   }
   const int nk = __popc(kb);
-  const int incl = block_inclusive_scan<false>(nk, scan);
-  int run = incl - nk;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    excl[4 * tid + j] = run;
-    run += (kb >> j) & 1u;
+
+  // one exchange between the waves: each wave's count before the tile and its
+  // kept tokens in the tile
+  int nk_incl = nk;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(nk_incl, o);
+    if (lane >= o) nk_incl += x;
   }
-  if (tid == kDirectThreads - 1) excl[kDirectTile] = run;
+  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+  if (lane == 63) {
+    red_c[wid] = c;
+    red_k[wid] = nk_incl;
+  }
   __syncthreads();
-  const int32_t prefix = s_prefix;
+  int32_t prefix = 0, wave_off = 0;
+  for (int w = 0; w < kDirectThreads / kWave; ++w) {
+    prefix += red_c[w];
+    if (w < wid) wave_off += red_k[w];
+  }
+  int run = wave_off + nk_incl - nk;   // kept tokens of the tile before this thread's first
   {
-    int k = prefix + incl - nk;
+    int k = prefix + run;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      excl[4 * tid + j] = run;
       if ((kb >> j) & 1u) {
         const int64_t i = i0 + j;
         a.index_out[k] = a.index_in ? a.index_in[i] : (int32_t)i;
         a.src_pos[k] = (int32_t)i;
         ++k;
+        ++run;
       }
     }
   }
-  // new request offsets that fall inside this tile (the last tile also owns T)
+  if (tid == kDirectThreads - 1) excl[kDirectTile] = run;
+  __syncthreads();
+
+  // new request offsets that fall inside this tile (the last tile also owns T):
+  // the clamped running maximum of cu, by one wave when it covers every entry
+  if (R < kWave) {
+    if (wid == 0) {
+      int32_t p = lane <= R ? clamp_cu(a.cu_in[lane], cap) : 0;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int32_t x = __shfl_up(p, o);
+        if (lane >= o) p = max(p, x);
+      }
+      if (lane <= R && p >= start && (p < end || (p == T && end == T))) a.cu_out[lane] = prefix + excl[p - start];
+    }
+    return;
+  }
+  if (tid == 0) s_carry = 0;
   for (int base = 0; base <= R; base += kDirectThreads) {
     const int e = base + tid;
     const int32_t v = (e <= R) ? clamp_cu(a.cu_in[e], cap) : 0;
