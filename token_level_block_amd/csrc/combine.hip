@@ -12,7 +12,9 @@
 namespace up {
 
 // ---------------------------------------------------------------------------
-// prep: clamp cu_seqlens and build block / chunk prefix offsets (one workgroup)
+// prep: clamp cu_seqlens and build block / chunk prefix offsets (one workgroup;
+// used for more than 63 requests and for selection from given scores, since
+// the score kernel derives them itself for smaller batches)
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 1024;
 constexpr int kPrepWaves = kPrepThreads / kWave;

@@ -2,15 +2,17 @@
 // (UniPrefill Sec. 3.4 Eq. 7-8; Sec. 3.5, the compacted stream that the
 // patched query_start_loc describes).
 //
-//   count  : one workgroup per 4096-token tile counts the set mask bytes;
-//   rank   : one workgroup per 256-token tile adds up the counts before it,
-//            ranks its kept tokens (wave ballots) and writes the index map,
-//            the stream position of every kept row and the new request
-//            offsets (of the clamped, non-decreasing cu_seqlens) that fall in
-//            its tile;
-//   copy   : waves spread evenly over the kept rows copy each row of every
-//            buffer with coalesced 16-byte accesses (the same kernel moves the
-//            rows back for the Eq. 8 scatter).
+//   rank_direct (streams of at most 131072 tokens): one workgroup per
+//            4096-token tile counts the kept tokens before its tile from the
+//            mask itself, ranks its own, and writes the index map, the stream
+//            position of every kept row and the new request offsets (of the
+//            clamped, non-decreasing cu_seqlens) that fall in its tile;
+//   count + rank (longer streams): the same in two launches, the first
+//            counting each 4096-token tile, the second (256-token tiles)
+//            adding up the counts before its tile;
+//   copy   : every buffer's kept rows in one launch; wide rows as one flat
+//            stream of 16-byte units in chip-wide order (the same kernel moves
+//            the rows back for the Eq. 8 scatter).
 // No atomics and no inter-workgroup waiting: every result is deterministic.
 #include "common.h"
 #include "copy_plan.h"
