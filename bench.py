@@ -260,7 +260,9 @@ def run_sweep(args, ev, stream):
            base,
            # the window ablation of UniPrefill Table 4 at 128K: n = 32 and 512
            *(replace(base, n=n, name=f"llama8b_128k_n{n}") for n in (32, 512)),
-           synth.serving_16x128k()]
+           synth.serving_16x128k(),
+           # the second drop layer of the serving batch: a selection on the compacted stream
+           synth.serving_16x128k(lengths=synth.serving_16x128k_layer1_lengths(), layer=1)]
     records = []
     for wl in wls:
         log(f"[sweep] {wl.name}: {wl.num_reqs} request(s), {sum(wl.lengths)} tokens")
