@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <initializer_list>
 
 #include "../token_level_block_amd/csrc/score_plan.h"
 
@@ -23,12 +24,13 @@ static int failures = 0;
     }                                                        \
   } while (0)
 
-static void pin(int d, int hq, int hkv, int n, int G, int64_t T, int nw, int nt, int zs, int per_cu, int chunk) {
+static void pin(int d, int hq, int hkv, int n, int G, int64_t T, int R, int nw, int nt, int zs, int per_cu,
+                int chunk) {
   const up::ScoreLaunch L = up::score_launch_for(d, hq, hkv, n);
-  const int32_t ck = up::chunk_keys_for(G, d, hq, hkv, n, T);
+  const int32_t ck = up::chunk_keys_for(G, d, hq, hkv, n, T, R);
   CHECK(L.nw == nw && L.nt == nt && L.zsplit == zs && L.per_cu == per_cu && ck == chunk,
-        "d=%d hq=%d hkv=%d n=%d G=%d T=%lld: plan {%d,%d,%d,%d} chunk %d, expected {%d,%d,%d,%d} chunk %d", d, hq,
-        hkv, n, G, (long long)T, L.nw, L.nt, L.zsplit, L.per_cu, ck, nw, nt, zs, per_cu, chunk);
+        "d=%d hq=%d hkv=%d n=%d G=%d T=%lld R=%d: plan {%d,%d,%d,%d} chunk %d, expected {%d,%d,%d,%d} chunk %d", d,
+        hq, hkv, n, G, (long long)T, R, L.nw, L.nt, L.zsplit, L.per_cu, ck, nw, nt, zs, per_cu, chunk);
 }
 
 int main() {
@@ -56,25 +58,32 @@ int main() {
         CHECK((qn + per_slice - 1) / per_slice == L.zsplit, "in-kernel slice count differs for qn=%lld",
               (long long)qn);
         for (int G : Gs)
-          for (int64_t T : Ts) {
-            const int32_t ck = up::chunk_keys_for(G, d, hq, hkv, n, T);
-            const int32_t base = G >= 128 ? G : G * ((128 + G - 1) / G);
-            const int32_t cap = base > 16384 ? base : 16384;
-            CHECK(ck % G == 0, "chunk %d not a multiple of G=%d", ck, G);
-            CHECK(ck >= base && ck <= cap, "chunk %d outside [%d, %d] (G=%d T=%lld)", ck, base, cap, G,
-                  (long long)T);
-            CHECK(ck % base == 0, "chunk %d not a multiple of the one-stage length %d", ck, base);
-            ++checked;
-          }
+          for (int64_t T : Ts)
+            for (int R : {0, 1, 2, 16}) {
+              const int32_t ck = up::chunk_keys_for(G, d, hq, hkv, n, T, R);
+              const int32_t base = G >= 128 ? G : G * ((128 + G - 1) / G);
+              const int32_t limit = R > 1 ? 4096 : 16384;
+              const int32_t cap = base > limit ? base : limit;
+              CHECK(ck % G == 0, "chunk %d not a multiple of G=%d", ck, G);
+              CHECK(ck >= base && ck <= cap, "chunk %d outside [%d, %d] (G=%d T=%lld R=%d)", ck, base, cap, G,
+                    (long long)T, R);
+              // more requests never lengthen the chunk
+              if (R > 1) CHECK(ck <= up::chunk_keys_for(G, d, hq, hkv, n, T, 1), "chunk grows with R=%d", R);
+              CHECK(ck % base == 0, "chunk %d not a multiple of the one-stage length %d", ck, base);
+              ++checked;
+            }
       }
   // the measured workloads (benchmark, sweep, ablations)
-  pin(128, 32, 8, 128, 64, 131072, 8, 2, 1, 1, 4096);      // LLaMA-3.1-8B-shaped 128K layer
-  pin(128, 32, 8, 128, 64, 4096, 8, 2, 1, 1, 128);         // its 4K request
-  pin(128, 32, 8, 32, 64, 131072, 4, 1, 1, 2, 2048);       // n = 32 window
-  pin(128, 32, 8, 512, 64, 131072, 8, 2, 4, 1, 16384);     // n = 512 window
-  pin(256, 16, 2, 128, 64, 65536, 8, 2, 2, 1, 1024);      // Qwen3-Next-shaped 64K layer
-  pin(256, 16, 8, 128, 64, 65536, 8, 1, 1, 1, 2048);      // Gemma-3-shaped 64K layer
-  pin(128, 32, 8, 128, 64, 2097152, 8, 2, 1, 1, 16384);    // 16 x 128K serving batch
+  pin(128, 32, 8, 128, 64, 131072, 1, 8, 2, 1, 1, 4096);      // LLaMA-3.1-8B-shaped 128K layer
+  pin(128, 32, 8, 128, 64, 4096, 1, 8, 2, 1, 1, 128);         // its 4K request
+  pin(128, 32, 8, 128, 64, 30720, 4, 8, 2, 1, 1, 1024);       // four ragged requests, 30K tokens
+  pin(128, 32, 8, 32, 64, 131072, 1, 4, 1, 1, 2, 2048);       // n = 32 window
+  pin(128, 32, 8, 512, 64, 131072, 1, 8, 2, 4, 1, 16384);     // n = 512 window
+  pin(256, 16, 2, 128, 64, 65536, 1, 8, 2, 2, 1, 1024);       // Qwen3-Next-shaped 64K layer
+  pin(256, 16, 8, 128, 64, 65536, 1, 8, 1, 1, 1, 2048);       // Gemma-3-shaped 64K layer
+  pin(128, 32, 8, 128, 64, 2097152, 16, 8, 2, 1, 1, 4096);    // 16 x 128K serving batch
+  pin(128, 32, 8, 128, 64, 1099200, 16, 8, 2, 1, 1, 4096);    // its second drop layer (ragged)
+  pin(128, 32, 8, 128, 64, 2097152, 1, 8, 2, 1, 1, 16384);    // one 2M-token request
   if (failures) {
     std::fprintf(stderr, "%d failures\n", failures);
     return 1;

@@ -49,7 +49,7 @@ up_status plan_select(const up_select_params* prm, int32_t R, int64_t max_tokens
   const int32_t G = prm->block_size;
   L->scoring = (prm->flags & UP_SCORES_IN) == 0u;
   L->chunk_keys = up::chunk_keys_for(G, prm->head_dim, prm->num_heads_q, prm->num_heads_kv, prm->window,
-                                     max_tokens);
+                                     max_tokens, R);
   L->max_blocks = max_tokens / G + R;
   L->max_chunks = max_tokens / L->chunk_keys + R;
   if (L->max_chunks > INT32_MAX) return UP_ERR_SHAPE;   // one top-p workgroup per chunk
