@@ -85,6 +85,9 @@ int main() {
         }
       }
       CHECK(p.wg_begin[0] == 0 && p.wg_begin[up::kMaxCopyBuffers] == p.wg_begin[nb], "range ends");
+      // the launch's threads fit the grid's 32-bit work-item count
+      CHECK((int64_t)p.wg_begin[nb] * up::kCopyThreads < (int64_t(1) << 32), "%lld workgroups",
+            (long long)p.wg_begin[nb]);
     }
   CHECK(!up::make_copy_plan(up::kMaxCopyBuffers + 1, nullptr, nullptr, 1, nullptr), "too many buffers");
 
@@ -103,9 +106,10 @@ int main() {
     const int32_t vg[] = {1};
     up::make_copy_plan(1, rg, vg, 65536, &p);
     CHECK(p.flat[0] == 1 && p.units[0] == 480 && p.wg_begin[1] == 65536 * 480 / 1024, "Gemma plan");
-    // 16 x 128K rows of 8 KiB: the cap
+    // 16 x 128K rows of 8 KiB: still a thread per four units (the cap, exactly)
     up::make_copy_plan(2, rb, v16, 2097152, &p);
-    CHECK(p.flat[0] == 1 && p.wg_begin[1] == up::kCopyFlatMaxGroups, "16 x 128K plan");
+    CHECK(p.flat[0] == 1 && p.wg_begin[1] == 2097152 * 512 / 1024 && p.wg_begin[1] == up::kCopyFlatMaxGroups,
+          "16 x 128K plan: %d groups", p.wg_begin[1]);
   }
   if (failures) return 1;
   std::printf("ok %ld\n", checks);

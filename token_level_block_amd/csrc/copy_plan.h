@@ -40,7 +40,7 @@ constexpr uint32_t fastdiv(uint32_t n, FastDiv f) {
 constexpr int kMaxCopyBuffers = 8;
 constexpr int kCopyThreads = 256;
 constexpr int64_t kCopyNarrowRow = 32;          // rows up to this many bytes go one per thread
-constexpr int64_t kCopyFlatMaxGroups = 65536;   // workgroups of one flat-copied buffer, at most
+constexpr int64_t kCopyFlatMaxGroups = 1 << 20;   // workgroups of one flat-copied buffer, at most
 
 // Per-buffer workgroup ranges of one copy launch: buffer b owns workgroups
 // [wg_begin[b], wg_begin[b+1]).  A buffer whose rows are 16-byte multiples
@@ -53,10 +53,14 @@ constexpr int64_t kCopyFlatMaxGroups = 65536;   // workgroups of one flat-copied
 // stream more slowly (8 KiB rows, 40 % of 131072 kept: 136 us at 16.8 M
 // threads, 144 us at 4.2 M; four units per thread per step: 164 us).  So a
 // buffer gets one thread per four 16-byte units of every row the call may
-// copy, at most kCopyFlatMaxGroups workgroups (beyond that they loop: 16 x
-// 131072 rows at 52 % kept, 33 steps, ~5.5 TB/s).  Flat needs max_rows *
-// units to fit 32 bits; other buffers copy a row per thread (narrow rows) or
-// per wave.
+// copy.  The same rule holds for long streams: a grid held to 65536
+// workgroups makes each thread loop over the stream (16 x 131072 rows of
+// 8 KiB at 52 % kept: 33 steps, 5.3 TB/s), and a plain copy measured the
+// same way drops from 6.45 TB/s in one pass to 5.2 TB/s once it loops over
+// more than 4 GiB.  The cap of 2^20 workgroups (2^28 threads) covers every
+// stream the flat path takes, which needs max_rows * units below 2^32, and
+// keeps the launch of eight such buffers under 2^31 threads.  Other buffers
+// copy a row per thread (narrow rows) or per wave.
 struct CopyPlan {
   int32_t wg_begin[kMaxCopyBuffers + 1];
   int32_t flat[kMaxCopyBuffers];
