@@ -4,7 +4,8 @@
 //
 // One workgroup owns (request, chunk of keys, KV head, slice of queries).  The
 // window queries of every query head that shares the KV head (GQA) are held in
-// registers as the B operand of v_mfma_f32_32x32x16_bf16.  K streams through
+// registers as the B operand of v_mfma_f32_32x32x16_bf16 (at d = 128 they
+// arrive through LDS in the K rows' layout, so their loads are coalesced).  K streams through
 // a double-buffered LDS ring with gfx950's direct global-to-LDS 16-byte loads
 // (no staging registers, XOR-swizzled rows so the A-operand reads are free of
 // bank conflicts) and feeds the A operand, so each 32x32 accumulator tile has
@@ -47,6 +48,16 @@ struct ScoreCfg {
   static constexpr int KPI = 1024 / ROWB;            // keys per 1 KB wave load
   static constexpr int NPW = STAGE / 1024 / NW;      // 1 KB wave loads per wave per stage
   static_assert(STAGE % (1024 * NW) == 0, "a stage must split evenly into 1 KB wave loads");
+  // Window queries staged through LDS at start-up: each wave's 32-query tiles
+  // land in the second K buffer (idle until the first stage prefetches into
+  // it) and a region after the ring, wherever the workgroups a CU holds still
+  // fit in its 160 KB.  Row loads then fill whole cache lines, where loads in
+  // the MFMA operand layout touch 32 lines each (128K layer: 1.5 us faster).
+  static constexpr int TILEB = 32 * ROWB;            // bytes of one 32-query tile
+  static constexpr int QBYTES = NW * NT * TILEB;
+  static constexpr int QR = QBYTES > STAGE ? QBYTES - STAGE : 0;
+  static constexpr int WGCU = NW == 4 ? 2 : 1;        // workgroups per CU (launch bounds)
+  static constexpr bool QLDS = (2 * STAGE + QR) * WGCU <= 160 * 1024;
 };
 
 template <int V> struct IntC { static constexpr int value = V; };
@@ -108,7 +119,7 @@ constexpr float kRescaleAbove = 1048576.0f;   // 2^20
 template <int D, int NW, int GT, int NT>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void score_kernel(ScoreArgs a) {
   using C = ScoreCfg<D, NW, NT>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE + (C::QLDS ? C::QR : 0)];
 
   // Grid x enumerates (key chunk, query slice).  Workgroups are dealt to the
   // 8 XCDs round-robin by id, so ids 8 apart share an XCD and its L2: the
@@ -187,6 +198,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void score_kernel(ScoreAr
   int qrow[C::NT];      // output row h*n + t, or -1 if the lane's query is padding
   int qlim[C::NT];      // last visible key (request-relative), -1 if none
   bf16x8 qf[C::NT][C::KSTEPS];
+  const int lkey = lane / C::PPR, lslot = lane % C::PPR;
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) {
     const int qi = qbase + nt * 32 + (lane & 31);
@@ -195,19 +207,70 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void score_kernel(ScoreAr
     const int h = j * gq + hh;
     qrow[nt] = valid ? h * n + t : -1;
     qlim[nt] = valid ? (N - ne + t) : -1;
-    const uint16_t* qp = a.q + (int64_t)(s + N - ne + t) * a.q_stride + (int64_t)h * D + half * 8;
+    if constexpr (!C::QLDS) {
+      const uint16_t* qp = a.q + (int64_t)(s + N - ne + t) * a.q_stride + (int64_t)h * D + half * 8;
 #pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (valid) v = *reinterpret_cast<const u32x4*>(qp + kk * 16);
-      qf[nt][kk] = __builtin_bit_cast(bf16x8, v);
+      for (int kk = 0; kk < C::KSTEPS; ++kk) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (valid) v = *reinterpret_cast<const u32x4*>(qp + kk * 16);
+        qf[nt][kk] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  }
+  // tile nt of this wave: LDS address of its 32 query rows (the region after
+  // the ring, then the ring's second buffer)
+  auto qtile = [&](int nt) -> uint8_t* {
+    const int q = nt * nwaves + wid;
+    return q * C::TILEB < C::QR ? smem + 2 * C::STAGE + q * C::TILEB : smem + C::STAGE + (q * C::TILEB - C::QR);
+  };
+  // a tile whose 32 queries are all valid and rows of one query head
+  // (wave-uniform)
+  auto tile_full = [&](int nt) -> bool {
+    const int f = qbase + nt * 32;
+    return f + 32 <= qn && f - (f / n) * n + 32 <= ne;
+  };
+  if constexpr (C::QLDS) {
+    // rows of each tile as K rows are staged: wave load i holds rows KPI*i ..
+    // KPI*i + KPI-1, lane slot lslot holds piece lslot ^ (row & SWZ).  A full
+    // tile is 32 consecutive window rows of one head; otherwise each row is
+    // placed on its own, and a row past the window or the last query re-reads
+    // the first window query (zeroed after the read)
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      if (tile_full(nt)) {
+        const int f = qbase + nt * 32, hf = f / n, tf = f - hf * n;
+        const uint16_t* tb = a.q + (int64_t)(s + N - ne + tf) * a.q_stride + (int64_t)(j * gq + hf) * D;
+#pragma unroll
+        for (int i = 0; i < 32 / C::KPI; ++i) {
+          const int rr = C::KPI * i + lkey;
+          const int p = lslot ^ (rr & C::SWZ);
+          __builtin_amdgcn_global_load_lds((const void*)(tb + (int64_t)rr * a.q_stride + p * 8),
+              (__attribute__((address_space(3))) void*)(qtile(nt) + i * 1024), 16, 0, 0);
+        }
+        continue;
+      }
+      const int qi0 = qbase + nt * 32 + lkey;
+      int hh = qi0 / n, t = qi0 - (qi0 / n) * n;
+#pragma unroll
+      for (int i = 0; i < 32 / C::KPI; ++i) {
+        if (i > 0) {
+          t += C::KPI;
+          while (t >= n) { t -= n; ++hh; }
+        }
+        const int rr = C::KPI * i + lkey;
+        const bool valid = (qi0 + C::KPI * i < qn) && (t < ne);
+        const int tt = valid ? t : 0, h = j * gq + (valid ? hh : 0);
+        const int p = lslot ^ (rr & C::SWZ);
+        const uint16_t* g = a.q + (int64_t)(s + N - ne + tt) * a.q_stride + (int64_t)h * D + p * 8;
+        __builtin_amdgcn_global_load_lds((const void*)g,
+            (__attribute__((address_space(3))) void*)(qtile(nt) + i * 1024), 16, 0, 0);
+      }
     }
   }
 
   // ---- K staging: direct global -> LDS loads (16 bytes per lane) ----
   // wave load c of a stage fills LDS bytes [c KB, c KB + 1 KB): keys KPI*c + lane/PPR,
   // slot lane%PPR, which holds piece slot ^ (key & SWZ) of that key (XOR swizzle)
-  const int lkey = lane / C::PPR, lslot = lane % C::PPR;
   const uint16_t* kbase = a.k + (int64_t)s * a.k_stride + (int64_t)j * D;
   auto load_stage = [&](int kb, int buf) {
 #pragma unroll
@@ -328,6 +391,28 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void score_kernel(ScoreAr
   const int nstages = (k1 - k0 + C::KT - 1) / C::KT;
   load_stage(k0, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if constexpr (C::QLDS) {
+    // this wave's query tiles have landed (its own loads): B fragments in the
+    // MFMA operand layout, read like the A fragments (row lane&31, piece
+    // kk*2 + half, swizzled); padding and out-of-window lanes get zeros
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+      const uint8_t* rowp = qtile(nt) + arow * C::ROWB;
+#pragma unroll
+      for (int kk = 0; kk < C::KSTEPS; ++kk) {
+        const int slot = (kk * 2 + half) ^ aswz;
+        qf[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(rowp + (slot << 4)));
+      }
+      if (!tile_full(nt)) {
+        // padding and out-of-window lanes get zeros
+#pragma unroll
+        for (int kk = 0; kk < C::KSTEPS; ++kk)
+          if (qrow[nt] < 0) qf[nt][kk] = bf16x8{};
+      }
+    }
+  }
+  // every wave's fragment reads are done before the first stage prefetches
+  // into the second buffer
   __syncthreads();
 
   floatx16 acc[C::NT];
