@@ -148,6 +148,18 @@ def test_select_random_shapes(seed):
     check_select(random_case(seed), label=f"random {seed}")
 
 
+# window-query tiles that straddle two query heads (n = 100), pad past the last
+# query, or hold rows past a short request's window: the per-row path of the
+# score kernel's staged query loads, at d = 128 with eight waves of two tiles
+# and at d = 256 with eight waves of one tile
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (16, 8, 256)], ids=["d128_two_tiles", "d256_one_tile"])
+def test_select_query_tiles_straddle_heads(hq, hkv, d):
+    wl = synth.tiny((3000, 57, 1200, 99), hq=hq, hkv=hkv, d=d, G=64, A=64, n=100, p=0.95, seed=51,
+                    kind="powerlaw", c=1.4)
+    ref, got, mism = check_select(wl, label=f"straddle d={d}")
+    say(f"  kept={got['kept'].tolist()} mismatched={mism}")
+
+
 def test_select_repeatable():
     wl = synth.tiny((3000, 900), hq=8, hkv=2, d=128, G=64, A=128, n=128, p=0.99, seed=7, kind="powerlaw", c=1.4)
     cu, q, k = synth.make_qk(wl)
