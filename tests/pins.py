@@ -295,6 +295,79 @@ def check_expand_invariants(impl):
         assert np.array_equal(m[free].astype(bool), kb[i[free] // G])
 
 
+def f32_nearest_even(fr):
+    """float32 nearest to the exact rational fr, ties to the even significand
+    (a test helper: RNE from the exact value, not through float64).  Also
+    returns whether fr lies within 1e-12 (relative) of a rounding midpoint,
+    where an inexact float64 intermediate could round the other way."""
+    x = np.float32(float(fr))
+    cands = [np.nextafter(x, np.float32(-np.inf)), x, np.nextafter(x, np.float32(np.inf))]
+    dist = [abs(Fraction(float(c)) - fr) for c in cands]
+    best = min(dist)
+    near = [c for c, dd in zip(cands, dist) if dd == best]
+    if len(near) > 1:
+        near = [c for c in near if int(np.array(c, np.float32).view(np.uint32)) % 2 == 0]
+    lo = max(c for c in cands if Fraction(float(c)) <= fr)
+    hi = np.nextafter(lo, np.float32(np.inf))
+    mid = (Fraction(float(lo)) + Fraction(float(hi))) / 2
+    return np.float32(near[0]), abs(fr - mid) <= Fraction(1, 10 ** 12) * abs(fr)
+
+
+def _select_fixture_common(res, g, case):
+    """Outputs of select shared by both modes of the two-request fixture."""
+    T = g["cu_seqlens"][-1]
+    assert np.asarray(res["block_offsets"]).tolist() == g["block_offsets"], res["block_offsets"]
+    assert np.asarray(res["keep_block"]).astype(int).tolist() == case["keep_block"], res["keep_block"]
+    mask = np.asarray(res["mask"])
+    assert mask.dtype == np.uint8 and len(mask) == T
+    assert mask.tolist() == case["mask"], mask.tolist()
+    assert np.asarray(res["kept"]).tolist() == case["kept"], res["kept"]
+
+
+def check_select_scores_in(impl):
+    """select() from given fp32 scores on two packed requests, the first at a
+    nonzero stream offset, the second no longer than A + n: per-request block
+    offsets (ceil(N/G), the second block partial), top-p per request, the
+    expanded mask placed at each request's stream offset, and kept counts that
+    include the forced sink and window tokens."""
+    g = load_golden("select_two_requests.json")
+    c = g["scores_in"]
+    b = np.array(c["scores_times_64"], dtype=np.float32) / np.float32(64)
+    res = impl.select(None, None, np.array(g["cu_seqlens"], np.int32), 1, 1, 8, g["G"], g["A"], g["n"],
+                      c["p"], scores_in=b)
+    _select_fixture_common(res, g, c)
+    b32 = np.asarray(res["b32"])
+    assert b32.dtype == np.float32 and np.array_equal(b32.view(np.uint32), b.view(np.uint32))
+
+
+def check_select_q_zero(impl):
+    """select() end to end with Q = 0 (closed-form uniform softmax) on the same
+    two packed requests: fp64 block scores equal the hand-worked fractions,
+    the fp32 scores handed to top-p are their round-to-nearest-even values,
+    and equal scores are ranked larger block index first."""
+    g = load_golden("select_two_requests.json")
+    c = g["q_zero"]
+    cu = np.array(g["cu_seqlens"], np.int32)
+    T = int(cu[-1])
+    hq, hkv, d = c["num_heads_q"], c["num_heads_kv"], c["head_dim"]
+    q = np.zeros((T, hq, d), np.uint16)
+    k = bf16_bits(np.random.default_rng(40).standard_normal((T, hkv, d)) * 2.0)
+    res = impl.select(q, k, cu, hq, hkv, d, g["G"], g["A"], g["n"], c["p"])
+    _select_fixture_common(res, g, c)
+    exact = [Fraction(s) / c["scale_denominator"] for s in c["block_sums"]]
+    b64 = np.asarray(res["b64"], dtype=np.float64)
+    assert np.allclose(b64, [float(x) for x in exact], rtol=1e-14, atol=0), b64
+    b32 = np.asarray(res["b32"])
+    assert b32.dtype == np.float32, b32.dtype
+    for i, x in enumerate(exact):
+        want, near_mid = f32_nearest_even(x)
+        assert not near_mid, "fixture value too close to a float32 rounding midpoint"
+        assert b32[i].view(np.uint32) == want.view(np.uint32), (i, b32[i], want)
+
+
+SELECT_CHECKS = [check_select_scores_in, check_select_q_zero]
+
+
 TOPP_CHECKS = [check_topp_fixture, check_topp_bruteforce, check_eq6_and_minimality,
                check_phi, check_topp_edges, check_expand_fixture, check_expand_invariants]
 
@@ -551,4 +624,4 @@ def check_ffn_rows_independent(impl):
 FFN_CHECKS = [check_ffn_fixture, check_silu, check_ffn_saturated_gates, check_ffn_linearity,
               check_ffn_rows_independent]
 
-ALL_CHECKS = SCORE_CHECKS + TOPP_CHECKS + COMPACT_CHECKS + SLOT_CHECKS + FFN_CHECKS
+ALL_CHECKS = SCORE_CHECKS + TOPP_CHECKS + SELECT_CHECKS + COMPACT_CHECKS + SLOT_CHECKS + FFN_CHECKS

@@ -276,6 +276,29 @@ def test_topp_fixture_through_gpu():
     assert int(bufs.kept[0]) == g["kept_tokens"]
 
 
+def test_select_two_request_fixture_through_gpu():
+    """The hand-worked two-request fixture that pins oracle.select (stream
+    offset 5, a request no longer than A + n) through the C ABI from its fp32
+    scores: offsets, flags, mask placement and kept counts as worked by hand."""
+    from pins import load_golden
+    g = load_golden("select_two_requests.json")
+    c = g["scores_in"]
+    sc = np.array(c["scores_times_64"], np.float32) / np.float32(64)
+    cu = np.array(g["cu_seqlens"], np.int32)
+    T = int(cu[-1])
+    prm = tlb.make_params(1, 1, 1, g["G"], g["A"], g["n"], c["p"], scores_in=True)
+    bufs = SelectBuffers.allocate(prm, 2, T)
+    bufs.keep_mask.fill_(0xAB)
+    bufs.run(None, None, dev(cu), scores_in=dev(sc))
+    torch.cuda.synchronize()
+    assert bufs.block_offsets[:3].cpu().tolist() == g["block_offsets"]
+    assert bufs.keep_block[:8].cpu().tolist() == c["keep_block"]
+    # tokens before the first request belong to no request: left untouched
+    assert bufs.keep_mask[:5].cpu().tolist() == [0xAB] * 5
+    assert bufs.keep_mask[5:T].cpu().tolist() == c["mask"][5:]
+    assert bufs.kept[:2].cpu().tolist() == c["kept"]
+
+
 # ---------------------------------------------------------------------------
 # compaction, scatter-back, metadata: bit-exact
 # ---------------------------------------------------------------------------

@@ -214,6 +214,53 @@ def _ffn_variant(act="silu", swap=False, no_up=False):
     return ffn_swiglu
 
 
+def _bf16_round(x):
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return (((b + (((b >> 16) & 1) + 0x7FFF)) >> 16) << 16).astype(np.uint32).view(np.float32)
+
+
+def _select_variant(mask_at_block_offsets=False, kept_before_forcing=False, rounding="f32",
+                    offsets="ceil", batch_topp=False):
+    """select() with one planted mistake: the mask written at the block offsets
+    instead of the stream offsets, kept counted from the top-p blocks before
+    the sinks and window are forced, the scores left in float64 or rounded to
+    bf16, block offsets by floor division or one too many per request, or
+    top-p taken over the whole batch instead of each request."""
+    def select(q_bits, k_bits, cu_seqlens, hq, hkv, d, G, A, n, p, scale=None, scores_in=None):
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        R = len(cu) - 1
+        if scores_in is None:
+            b64, _ = U.block_scores(q_bits, k_bits, cu, hq, hkv, d, G, n, scale)
+            b32 = {"f32": b64.astype(np.float32), "none": b64, "bf16": _bf16_round(b64)}[rounding]
+        else:
+            b64, b32 = None, np.ascontiguousarray(scores_in, dtype=np.float32)
+        offs = [0]
+        for r in range(R):
+            N = int(cu[r + 1] - cu[r])
+            nb = {"ceil": -(-N // G), "floor": N // G, "plus_one": N // G + 1}[offsets]
+            offs.append(offs[-1] + nb)
+        offs = np.asarray(offs, dtype=np.int64)
+        T = int(cu[-1])
+        mask = np.zeros(T, dtype=np.uint8)
+        keep_block = np.zeros(len(b32), dtype=np.uint8)
+        kept = np.zeros(R, dtype=np.int32)
+        whole = U.top_p_select(b32, p) if batch_topp else None
+        for r in range(R):
+            N = int(cu[r + 1] - cu[r])
+            kb = whole[offs[r]: offs[r + 1]] if batch_topp else U.top_p_select(b32[offs[r]: offs[r + 1]], p)
+            keep_block[offs[r]: offs[r + 1]] = kb
+            # a request's flags padded or cut to its true block count, so a
+            # wrong offset shows in the outputs rather than as a crash
+            kbx = np.zeros(-(-N // G), dtype=bool)
+            kbx[: min(len(kb), len(kbx))] = np.asarray(kb[: len(kbx)], dtype=bool)
+            m = U.expand_mask(kbx, N, G, A, n)
+            at = int(offs[r]) if mask_at_block_offsets else int(cu[r])
+            mask[at: at + N] = m[: max(0, min(N, T - at))]
+            kept[r] = int(sum(min(G, N - g * G) for g in np.nonzero(kbx)[0])) if kept_before_forcing else int(m.sum())
+        return dict(b64=b64, b32=b32, block_offsets=offs, keep_block=keep_block, mask=mask, kept=kept)
+    return select
+
+
 def _silu_sigmoid(z):
     return 1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64)))
 
@@ -248,6 +295,13 @@ MUTANTS = {
     "ffn_sigmoid_gate": _namespace(ffn_swiglu=_ffn_variant(act="sigmoid")),
     "ffn_no_up_projection": _namespace(ffn_swiglu=_ffn_variant(no_up=True)),
     "silu_is_sigmoid": _namespace(silu=_silu_sigmoid),
+    "select_mask_at_block_offsets": _namespace(select=_select_variant(mask_at_block_offsets=True)),
+    "select_kept_before_forcing": _namespace(select=_select_variant(kept_before_forcing=True)),
+    "select_scores_unrounded": _namespace(select=_select_variant(rounding="none")),
+    "select_scores_bf16": _namespace(select=_select_variant(rounding="bf16")),
+    "select_offsets_floor": _namespace(select=_select_variant(offsets="floor")),
+    "select_offsets_plus_one": _namespace(select=_select_variant(offsets="plus_one")),
+    "select_topp_over_batch": _namespace(select=_select_variant(batch_topp=True)),
 }
 
 
