@@ -360,11 +360,8 @@ def measure_step(wl, steps, warmup, ev, stream, pipelined=False):
 
     def step(s, marks=None):
         if marks is not None:
-            prm.prof_score_begin, prm.prof_score_end = marks["score"]
             ev.record(marks["t0"], s)
-        else:
-            prm.prof_score_begin = prm.prof_score_end = None
-        sel.run(qd, kd, cu_d, stream=s)
+        sel.run(qd, kd, cu_d, stream=s, score_events=None if marks is None else marks["score"])
         if marks is not None:
             ev.record(marks["t1"], s)
         cb.run(sel.keep_mask, cu_d, [hidden, pos], [out, pos_out], stream=s)
@@ -504,7 +501,6 @@ def measure_two_in_flight(steps, ev, stream, ref_out, kept_now, R, T, prm, cu_d,
         for st in streams:
             cur.wait_stream(st)
 
-    prm.prof_score_begin = prm.prof_score_end = None
     # new streams run slowly for their first few milliseconds of work (measured:
     # the first 20 rounds at 0.57-0.62 ms per batch, later ones at 0.36-0.39)
     rounds(max(steps, 20))

@@ -59,11 +59,6 @@ typedef struct up_select_params {
   double top_p;           /* 0 < p <= 1 (Eq. 5) */
   float softmax_scale;    /* <= 0 selects 1/sqrt(d) (Eq. 2) */
   uint32_t flags;         /* UP_SCORES_IN or 0 */
-  /* Optional profiling hooks (NULL = none): hipEvent_t handles that the call
-   * records on `stream` immediately before and after the score kernel, so a
-   * caller can time that kernel alone with hipEventElapsedTime. */
-  void* prof_score_begin;
-  void* prof_score_end;
 } up_select_params;
 
 /* Upper bound on sum_r ceil(N_r / G) for any batch of num_reqs requests and at

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include "uniprefill.h"
+#include "uniprefill_prof.h"
 
 #define FAKE ((void*)(1u << 20)) /* nonzero, aligned, never dereferenced */
 
@@ -20,8 +21,6 @@ int main(void) {
   prm.top_p = 0.99;
   prm.softmax_scale = 0.0f;
   prm.flags = 0u;
-  prm.prof_score_begin = NULL;
-  prm.prof_score_end = NULL;
 
   printf("max_blocks %lld\n", (long long)up_max_blocks(64, 1, 131072));
   printf("select_ws_positive %d\n", up_select_workspace_bytes(&prm, 1, 131072) > 0);
@@ -34,6 +33,9 @@ int main(void) {
   printf("select_bad_p %d\n",
          (int)up_select_blocks(&prm, FAKE, 4096, FAKE, 1024, FAKE, 1, 4096, NULL, FAKE, FAKE, FAKE, FAKE, FAKE,
                                FAKE, (size_t)1 << 30, NULL));
+  printf("select_profiled_bad_p %d\n",
+         (int)up_select_blocks_profiled(&prm, FAKE, 4096, FAKE, 1024, FAKE, 1, 4096, NULL, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, (size_t)1 << 30, NULL, NULL, NULL));
   prm.top_p = 0.99;
   printf("select_small_workspace %d\n",
          (int)up_select_blocks(&prm, FAKE, 4096, FAKE, 1024, FAKE, 1, 4096, NULL, FAKE, FAKE, FAKE, FAKE, FAKE,

@@ -2,6 +2,7 @@
 declares, sizes workspaces, and rejects bad arguments on the host before any
 launch (every call below fails validation, so no HIP work is attempted)."""
 import ctypes
+import glob
 import math
 import os
 import re
@@ -15,12 +16,14 @@ from conftest import ROOT
 tlb = pytest.importorskip("token_level_block_amd")
 
 HEADER = os.path.join(ROOT, "include", "uniprefill.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 FAKE = 1 << 20            # a nonzero, 256-aligned address that is never dereferenced
 FAKE_MIS = FAKE + 2       # misaligned
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    """Every up_* function declared in any include/*.h header."""
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(up_[a-z_]+)\s*\(", text)))
 
@@ -274,6 +277,7 @@ def test_header_is_plain_c(tmp_path):
         "status_ok": "set",
         "select_null_params": str(tlb.UP_ERR_NULL),
         "select_bad_p": str(tlb.UP_ERR_PARAM),
+        "select_profiled_bad_p": str(tlb.UP_ERR_PARAM),
         "select_small_workspace": str(tlb.UP_ERR_WORKSPACE),
         "scatter_odd_rows": str(tlb.UP_ERR_PARAM),
         "metadata_negative_layer": str(tlb.UP_ERR_SHAPE),

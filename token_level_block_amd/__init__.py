@@ -40,7 +40,7 @@ UP_ERR_ALIGN = -5
 UP_ERR_HIP = -6
 UP_SCORES_IN = 1
 
-EXPORTED = ("up_max_blocks", "up_select_workspace_bytes", "up_select_blocks",
+EXPORTED = ("up_max_blocks", "up_select_workspace_bytes", "up_select_blocks", "up_select_blocks_profiled",
             "up_compact_workspace_bytes", "up_compact", "up_scatter_back",
             "up_update_metadata", "up_slot_mapping", "up_write_kv_cache", "up_ffn_create",
             "up_ffn_destroy", "up_ffn_workspace_bytes", "up_ffn_forward", "up_status_string")
@@ -58,8 +58,6 @@ class SelectParams(ctypes.Structure):
         ("top_p", ctypes.c_double),
         ("softmax_scale", ctypes.c_float),
         ("flags", ctypes.c_uint32),
-        ("prof_score_begin", ctypes.c_void_p),
-        ("prof_score_end", ctypes.c_void_p),
     ]
 
 
@@ -79,6 +77,8 @@ _lib.up_select_workspace_bytes.argtypes = [ctypes.POINTER(SelectParams), _i32, _
 _lib.up_select_blocks.restype = ctypes.c_int
 _lib.up_select_blocks.argtypes = [ctypes.POINTER(SelectParams), _vp, _i64, _vp, _i64, _vp, _i32, _i64,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.up_select_blocks_profiled.restype = ctypes.c_int
+_lib.up_select_blocks_profiled.argtypes = _lib.up_select_blocks.argtypes + [_vp, _vp]
 _lib.up_compact_workspace_bytes.restype = _sz
 _lib.up_compact_workspace_bytes.argtypes = [_i32, _i64]
 _lib.up_compact.restype = ctypes.c_int
@@ -134,8 +134,7 @@ def status_string(status: int) -> str:
 def make_params(num_heads_q, num_heads_kv, head_dim, block_size=64, num_sink=128, window=128,
                 top_p=0.99, softmax_scale=0.0, scores_in=False) -> SelectParams:
     return SelectParams(num_heads_q, num_heads_kv, head_dim, block_size, num_sink, window,
-                        float(top_p), float(softmax_scale), UP_SCORES_IN if scores_in else 0,
-                        None, None)
+                        float(top_p), float(softmax_scale), UP_SCORES_IN if scores_in else 0)
 
 
 def max_blocks(block_size: int, num_reqs: int, max_tokens: int) -> int:
@@ -159,6 +158,23 @@ def select_blocks(params: SelectParams, q, q_row_stride, k, k_row_stride, cu_seq
                                _ptr(keep_mask), _ptr(kept_per_req), _ptr(workspace),
                                workspace_bytes, _stream(stream))
     return _check(st, "up_select_blocks", raise_on_error)
+
+
+def select_blocks_profiled(params: SelectParams, q, q_row_stride, k, k_row_stride, cu_seqlens, num_reqs,
+                           max_tokens, scores_in, block_scores, block_offsets, keep_block, keep_mask,
+                           kept_per_req, workspace, score_begin, score_end, workspace_bytes=None, stream=None,
+                           raise_on_error=True):
+    """up_select_blocks_profiled (include/uniprefill_prof.h): up_select_blocks plus
+    two hipEvent_t handles recorded right around the score kernel."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    pp = ctypes.byref(params) if params is not None else None
+    st = _lib.up_select_blocks_profiled(pp, _ptr(q), q_row_stride, _ptr(k), k_row_stride,
+                                        _ptr(cu_seqlens), num_reqs, max_tokens, _ptr(scores_in),
+                                        _ptr(block_scores), _ptr(block_offsets), _ptr(keep_block),
+                                        _ptr(keep_mask), _ptr(kept_per_req), _ptr(workspace),
+                                        workspace_bytes, _stream(stream), score_begin, score_end)
+    return _check(st, "up_select_blocks_profiled", raise_on_error)
 
 
 def compact_workspace_bytes(num_reqs: int, max_tokens: int) -> int:

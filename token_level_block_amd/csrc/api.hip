@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include "../../include/uniprefill.h"
+#include "../../include/uniprefill_prof.h"
 #include "common.h"
 #include "score_plan.h"
 
@@ -105,12 +106,19 @@ size_t up_select_workspace_bytes(const up_select_params* prm, int32_t num_reqs, 
   return L.total;
 }
 
-up_status up_select_blocks(const up_select_params* prm, const void* q, int64_t q_row_stride,
-                           const void* k, int64_t k_row_stride, const int32_t* cu_seqlens,
-                           int32_t num_reqs, int64_t max_tokens, const float* scores_in,
-                           float* block_scores, int32_t* block_offsets, uint8_t* keep_block,
-                           uint8_t* keep_mask, int32_t* kept_per_req, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// up_select_blocks, with optional events recorded on `stream` right before
+// and after the score kernel (instrumentation: up_select_blocks_profiled)
+up_status select_blocks_impl(const up_select_params* prm, const void* q, int64_t q_row_stride,
+                             const void* k, int64_t k_row_stride, const int32_t* cu_seqlens,
+                             int32_t num_reqs, int64_t max_tokens, const float* scores_in,
+                             float* block_scores, int32_t* block_offsets, uint8_t* keep_block,
+                             uint8_t* keep_mask, int32_t* kept_per_req, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream, hipEvent_t ev_begin,
+                             hipEvent_t ev_end) {
   SelectLayout L;
   up_status st = plan_select(prm, num_reqs, max_tokens, &L);
   if (st != UP_OK) return st;
@@ -171,11 +179,9 @@ up_status up_select_blocks(const up_select_params* prm, const void* q, int64_t q
     sa.cu_in = inline_offsets ? cu_seqlens : nullptr;
     sa.cap = (int32_t)max_tokens;
     sa.block_offsets_out = block_offsets;
-    if (prm->prof_score_begin && hipEventRecord((hipEvent_t)prm->prof_score_begin, stream) != hipSuccess)
-      return UP_ERR_HIP;
+    if (ev_begin != nullptr && hipEventRecord(ev_begin, stream) != hipSuccess) return UP_ERR_HIP;
     if (up::launch_score(sa, stream) != hipSuccess) return UP_ERR_HIP;
-    if (prm->prof_score_end && hipEventRecord((hipEvent_t)prm->prof_score_end, stream) != hipSuccess)
-      return UP_ERR_HIP;
+    if (ev_end != nullptr && hipEventRecord(ev_end, stream) != hipSuccess) return UP_ERR_HIP;
     up::CombineArgs ca;
     ca.off = off;
     ca.R = R;
@@ -211,6 +217,34 @@ up_status up_select_blocks(const up_select_params* prm, const void* q, int64_t q
   ta.max_chunks = L.max_chunks;
   if (up::launch_topp(ta, stream) != hipSuccess) return UP_ERR_HIP;
   return UP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+up_status up_select_blocks(const up_select_params* prm, const void* q, int64_t q_row_stride,
+                           const void* k, int64_t k_row_stride, const int32_t* cu_seqlens,
+                           int32_t num_reqs, int64_t max_tokens, const float* scores_in,
+                           float* block_scores, int32_t* block_offsets, uint8_t* keep_block,
+                           uint8_t* keep_mask, int32_t* kept_per_req, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  return select_blocks_impl(prm, q, q_row_stride, k, k_row_stride, cu_seqlens, num_reqs, max_tokens,
+                            scores_in, block_scores, block_offsets, keep_block, keep_mask, kept_per_req,
+                            workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+up_status up_select_blocks_profiled(const up_select_params* prm, const void* q, int64_t q_row_stride,
+                                    const void* k, int64_t k_row_stride, const int32_t* cu_seqlens,
+                                    int32_t num_reqs, int64_t max_tokens, const float* scores_in,
+                                    float* block_scores, int32_t* block_offsets, uint8_t* keep_block,
+                                    uint8_t* keep_mask, int32_t* kept_per_req, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream, void* score_begin,
+                                    void* score_end) {
+  return select_blocks_impl(prm, q, q_row_stride, k, k_row_stride, cu_seqlens, num_reqs, max_tokens,
+                            scores_in, block_scores, block_offsets, keep_block, keep_mask, kept_per_req,
+                            workspace, workspace_bytes, stream, static_cast<hipEvent_t>(score_begin),
+                            static_cast<hipEvent_t>(score_end));
 }
 
 size_t up_compact_workspace_bytes(int32_t num_reqs, int64_t max_tokens) {

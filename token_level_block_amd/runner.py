@@ -11,7 +11,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (SelectParams, compact, compact_workspace_bytes, make_params, max_blocks,
-               scatter_back, select_blocks, select_workspace_bytes, update_metadata)
+               scatter_back, select_blocks, select_blocks_profiled, select_workspace_bytes,
+               update_metadata)
 
 
 def _empty(n, dtype, device):
@@ -44,9 +45,16 @@ class SelectBuffers:
             workspace=_empty(ws, torch.uint8, device),
         )
 
-    def run(self, q, k, cu_seqlens, scores_in=None, stream=None):
+    def run(self, q, k, cu_seqlens, scores_in=None, stream=None, score_events=None):
+        """score_events: optional (begin, end) hipEvent_t handles recorded around
+        the score kernel (the instrumentation entry point)."""
         qs = q.stride(0) if q is not None else 0
         ks = k.stride(0) if k is not None else 0
+        if score_events is not None:
+            return select_blocks_profiled(self.params, q, qs, k, ks, cu_seqlens, self.num_reqs,
+                                          self.max_tokens, scores_in, self.block_scores, self.block_offsets,
+                                          self.keep_block, self.keep_mask, self.kept, self.workspace,
+                                          score_events[0], score_events[1], stream=stream)
         return select_blocks(self.params, q, qs, k, ks, cu_seqlens, self.num_reqs, self.max_tokens,
                              scores_in, self.block_scores, self.block_offsets, self.keep_block,
                              self.keep_mask, self.kept, self.workspace, stream=stream)
