@@ -238,7 +238,7 @@ def time_ffn(keep_mask, cu_d, R, T, kept, wl, stream, ev, reps=3):
             "ms_full": ms_full, "ms_kept": ms_kept,
             "tflops_full": flops(T) / (ms_full * 1e-3) / 1e12, "tflops_kept": flops(kept) / (ms_kept * 1e-3) / 1e12,
             "saving_measured": 1.0 - ms_kept / ms_full, "saving_eq10": 1.0 - kept / T,
-            "gemms": "hipBLASLt bf16, fp32 accumulate; SwiGLU in swiglu_kernel"}
+            "gemms": "ffn_gemm_kernel: bf16 MFMA 32x32x16, fp32 accumulate; SwiGLU fused into the gate/up epilogue"}
 
 
 def ratio(a, b):

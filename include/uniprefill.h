@@ -249,34 +249,28 @@ up_status up_write_kv_cache(const void* key, int64_t key_row_stride, const void*
  * rows, which is the saving Eq. 9-10 counts; calling it on the compacted
  * stream instead of the full one is that saving.
  *
- * up_ffn_create   host-side set-up for hidden width D and intermediate width F
- *                 (both positive multiples of 8): a hipBLASLt handle and GEMM
- *                 descriptors.  Unlike every other call it allocates (host
- *                 objects, and whatever hipBLASLt allocates for its handle);
- *                 create once, reuse.  UP_ERR_PARAM on bad widths, UP_ERR_HIP
- *                 if hipBLASLt fails.
- * up_ffn_destroy  releases it (NULL is a no-op).
- * up_ffn_workspace_bytes  device workspace up_ffn_forward needs for `rows`:
- *                 rows x 2F bf16 (gate/up product) + rows x F bf16 (activation)
- *                 + 64 MiB of GEMM scratch.
+ * up_ffn_workspace_bytes  device workspace up_ffn_forward needs for `rows`
+ *                 rows of hidden width D and intermediate width F (both
+ *                 positive multiples of 8, at most 2^24): the activation h,
+ *                 rows x F bf16, rounded up to 256 bytes.  0 if invalid.
  * up_ffn_forward  x bf16 [rows][D]; w_gate_up bf16 [2F][D] (gate rows, then up
  *                 rows: the [out][in] layout of a linear layer); w_down bf16
- *                 [D][F]; y bf16 out [rows][D].  GEMMs accumulate in fp32; the
- *                 gate/up product and the activation are rounded to bf16.
- *                 rows is a host value (e.g. the kept count read back once
- *                 the compaction has run); rows == 0 does nothing.  All
- *                 pointers 16-byte aligned.  One up_ffn must not be used by two
- *                 threads at once (it caches the GEMM choice for the last row
- *                 count).  Errors: UP_ERR_NULL, UP_ERR_SHAPE, UP_ERR_ALIGN,
- *                 UP_ERR_WORKSPACE, UP_ERR_HIP.
+ *                 [D][F]; y bf16 out [rows][D].  Products of bf16 inputs
+ *                 accumulate in fp32; silu(gate) * up is formed in fp32 from
+ *                 the two fp32 accumulators and rounded once to bf16 (h, kept
+ *                 in the workspace); y is rounded to bf16.  rows is a host
+ *                 value (e.g. the kept count read back once the compaction has
+ *                 run); rows == 0 does nothing.  All pointers 16-byte aligned;
+ *                 y must not overlap x or the workspace.  Like every other
+ *                 call it only enqueues work (no allocation, no handle, no
+ *                 state).  Errors: UP_ERR_PARAM (widths), UP_ERR_NULL,
+ *                 UP_ERR_SHAPE (rows < 0, or a grid past 32 bits),
+ *                 UP_ERR_ALIGN, UP_ERR_WORKSPACE, UP_ERR_HIP.
  */
-typedef struct up_ffn up_ffn;
-up_status up_ffn_create(int32_t hidden, int32_t intermediate, up_ffn** out);
-void up_ffn_destroy(up_ffn* ffn);
-size_t up_ffn_workspace_bytes(const up_ffn* ffn, int64_t rows);
-up_status up_ffn_forward(up_ffn* ffn, const void* x, int64_t rows, const void* w_gate_up,
-                         const void* w_down, void* y, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream);
+size_t up_ffn_workspace_bytes(int32_t hidden, int32_t intermediate, int64_t rows);
+up_status up_ffn_forward(int32_t hidden, int32_t intermediate, const void* x, int64_t rows,
+                         const void* w_gate_up, const void* w_down, void* y, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* up_status_string(up_status status);

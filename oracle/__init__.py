@@ -29,5 +29,6 @@ from .uniprefill_oracle import (  # noqa: F401
     slot_mapping,
     write_kv_cache,
     silu,
+    ffn_hidden,
     ffn_swiglu,
 )

@@ -340,15 +340,21 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def ffn_swiglu(x_bits, w_gate_up_bits, w_down_bits):
-    """Gated FFN of the LLaMA family (SwiGLU), token by token:
-        g = x Wg^T, u = x Wu^T, h = silu(g) * u, y = h Wd^T
-    x [rows, D], w_gate_up [2F, D] (gate rows first, then up rows),
-    w_down [D, F], all bf16 bit patterns; float64 throughout."""
+def ffn_hidden(x_bits, w_gate_up_bits):
+    """The gated FFN's activation, token by token: g = x Wg^T, u = x Wu^T,
+    h = silu(g) * u.  x [rows, D], w_gate_up [2F, D] (gate rows first, then
+    up rows), bf16 bit patterns; float64 [rows, F]."""
     x = bf16_bits_to_f64(np.asarray(x_bits))
     w = bf16_bits_to_f64(np.asarray(w_gate_up_bits))
-    wd = bf16_bits_to_f64(np.asarray(w_down_bits))
     F = w.shape[0] // 2
     g = x @ w[:F].T
     u = x @ w[F:].T
-    return (silu(g) * u) @ wd.T
+    return silu(g) * u
+
+
+def ffn_swiglu(x_bits, w_gate_up_bits, w_down_bits):
+    """Gated FFN of the LLaMA family (SwiGLU), token by token:
+        y = h Wd^T with h = silu(x Wg^T) * (x Wu^T) (ffn_hidden),
+    w_down [D, F] bf16 bit patterns; float64 throughout."""
+    wd = bf16_bits_to_f64(np.asarray(w_down_bits))
+    return ffn_hidden(x_bits, w_gate_up_bits) @ wd.T

@@ -555,6 +555,27 @@ def check_ffn_fixture(impl):
     y = impl.ffn_swiglu(bf16_bits(np.array([g["x"]])), bf16_bits(np.array(g["w_gate_up"])),
                         bf16_bits(np.array(g["w_down"])))
     assert np.allclose(y[0], g["y"], rtol=1e-15, atol=0), y
+    h = impl.ffn_hidden(bf16_bits(np.array([g["x"]])), bf16_bits(np.array(g["w_gate_up"])))
+    assert np.allclose(h[0], g["h"], rtol=1e-15, atol=0), h
+
+
+def check_ffn_hidden_composes(impl):
+    """y is the activation h times the down projection: ffn_swiglu equals
+    ffn_hidden @ Wd^T, and h = silu(x Wg^T) * (x Wu^T) channel by channel, so
+    a zero up row zeroes its channel and a zero gate row does too (silu(0) = 0)."""
+    rng = np.random.default_rng(35)
+    rows, D, F = 9, 16, 12
+    x, w, wd = _ffn_case(rng, rows, D, F)
+    h = impl.ffn_hidden(x, w)
+    assert h.shape == (rows, F)
+    assert np.allclose(impl.ffn_swiglu(x, w, wd), h @ bits_to_f64(wd).T, rtol=1e-13, atol=1e-15)
+    w0 = w.copy()
+    w0[F + 3] = 0          # up row of channel 3
+    w0[5] = 0              # gate row of channel 5
+    h0 = impl.ffn_hidden(x, w0)
+    assert np.all(h0[:, 3] == 0) and np.all(h0[:, 5] == 0)
+    keep = [c for c in range(F) if c not in (3, 5)]
+    assert np.array_equal(h0[:, keep], h[:, keep])
 
 
 def check_silu(impl):
@@ -622,6 +643,6 @@ def check_ffn_rows_independent(impl):
 
 
 FFN_CHECKS = [check_ffn_fixture, check_silu, check_ffn_saturated_gates, check_ffn_linearity,
-              check_ffn_rows_independent]
+              check_ffn_rows_independent, check_ffn_hidden_composes]
 
 ALL_CHECKS = SCORE_CHECKS + TOPP_CHECKS + SELECT_CHECKS + COMPACT_CHECKS + SLOT_CHECKS + FFN_CHECKS

@@ -245,14 +245,23 @@ def test_slot_mapping_and_kv_write_reject():
 
 
 def test_ffn_rejects_before_any_hip_work():
-    assert tlb.ffn_create_status(0, 64) == tlb.UP_ERR_PARAM
-    assert tlb.ffn_create_status(4096, 14330) == tlb.UP_ERR_PARAM     # not a multiple of 8
-    assert tlb.ffn_create_status(-8, 64) == tlb.UP_ERR_PARAM
     lib = tlb._lib
-    assert lib.up_ffn_create(64, 64, None) == tlb.UP_ERR_NULL
-    assert lib.up_ffn_workspace_bytes(None, 10) == 0
-    assert lib.up_ffn_forward(None, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == tlb.UP_ERR_NULL
-    lib.up_ffn_destroy(None)
+    assert lib.up_ffn_workspace_bytes(0, 64, 4) == 0
+    assert lib.up_ffn_workspace_bytes(4096, 14330, 4) == 0      # not a multiple of 8
+    assert lib.up_ffn_workspace_bytes(64, 64, -1) == 0
+    assert lib.up_ffn_workspace_bytes(64, 64, 10) >= 10 * 64 * 2
+    with pytest.raises(tlb.UniPrefillError):
+        tlb.FFN(-8, 64)
+    ws = 1 << 30
+    fwd = lambda *a: lib.up_ffn_forward(*a)
+    assert fwd(4096, 14330, FAKE, 4, FAKE, FAKE, FAKE, FAKE, ws, None) == tlb.UP_ERR_PARAM
+    assert fwd(64, 64, FAKE, -1, FAKE, FAKE, FAKE, FAKE, ws, None) == tlb.UP_ERR_SHAPE
+    assert fwd(64, 64, None, 4, FAKE, FAKE, FAKE, FAKE, ws, None) == tlb.UP_ERR_NULL
+    assert fwd(64, 64, FAKE, 4, FAKE, FAKE, None, FAKE, ws, None) == tlb.UP_ERR_NULL
+    assert fwd(64, 64, FAKE_MIS, 4, FAKE, FAKE, FAKE, FAKE, ws, None) == tlb.UP_ERR_ALIGN
+    assert fwd(64, 64, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 16, None) == tlb.UP_ERR_WORKSPACE
+    # zero rows: nothing to do, nothing read
+    assert fwd(64, 64, None, 0, None, None, None, None, 0, None) == tlb.UP_OK
 
 
 def test_header_is_plain_c(tmp_path):

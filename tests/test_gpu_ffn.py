@@ -3,12 +3,26 @@ sublayers run on the retained rows only) against the CPU oracle, and the
 Eq. 7 + Eq. 8 composition on the 128K LLaMA layer: compact the rows, run the
 FFN on the retained set, scatter back.
 
-Tolerance (floating point, derived from the arithmetic): the GPU multiplies
-bf16 inputs exactly and accumulates in fp32, but rounds the gate/up product
-and the activation h to bf16 (relative 2^-9 each) and y to bf16.  An error of
-a few 2^-9 on each of the F terms of y = h Wd^T, with random signs, gives a
-relative L2 error per row of about 5e-3; the bound is 1.5e-2 per row, and no
-element may be off by more than 0.05 of its row's rms (about 10 sigma).
+Tolerance, element by element, from the rounding steps of the GPU path (bf16
+inputs; products exact in fp32; every sum accumulated in fp32; h = silu(g) * u
+formed in fp32 from the fp32 gate and up sums, then rounded to bf16; y
+accumulated in fp32 and rounded to bf16).  With u = 2^-8 the unit roundoff of
+bf16 and Y, H the oracle's float64 output and activation, output element i of
+a row may differ from Y_i by at most
+    u |Y_i|                                  rounding of y to bf16,
+  + 7 (u / sqrt 3) sqrt(sum_f H_f^2 Wd_if^2)  rounding of each h_f to bf16: F
+                                             independent round-to-nearest errors
+                                             of at most u |H_f| (standard
+                                             deviation u/sqrt 3 relative), taken
+                                             at seven standard deviations,
+  + 2^-16 sum_f |H_f Wd_if|                  fp32 accumulation of the three
+                                             products and the fp32 SiLU: relative
+                                             errors of order sqrt(K) 2^-24 < 2^-16
+                                             on each term.
+Beside the per-element bound, the errors over a whole output, in units of the
+standard deviation this model predicts (the two bf16 roundings), must have an
+RMS below 1.5: an error that the rounding model does not explain fails even
+when each element stays inside its bound.
 """
 from __future__ import annotations
 
@@ -27,8 +41,10 @@ from token_level_block_amd.runner import CompactBuffers, run_scatter_back  # noq
 
 pytestmark = pytest.mark.gpu
 
-ROW_REL_L2 = 1.5e-2
-ELEM_OF_RMS = 0.05
+U_BF16 = 2.0 ** -8
+LAMBDA = 7.0
+SLACK_FP32 = 2.0 ** -16
+RMS_UNITS = 1.5
 
 
 def say(*a):
@@ -53,14 +69,26 @@ def gpu_ffn(ffn, x, rows, wg, wd):
 
 
 def check_rows(y_gpu, x_bits, wg_bits, wd_bits, where=""):
-    ref = oracle.ffn_swiglu(x_bits, wg_bits, wd_bits)
+    """Every element of every given row within the rounding bound; the RMS of
+    the errors in predicted standard deviations below RMS_UNITS."""
+    H = oracle.ffn_hidden(x_bits, wg_bits)
+    wd = oracle.bf16_bits_to_f64(np.asarray(wd_bits))
+    Y = H @ wd.T
     got = y_gpu.float().cpu().numpy().astype(np.float64)
-    for i in range(len(ref)):
-        rms = np.sqrt(np.mean(ref[i] ** 2))
-        rel = np.linalg.norm(got[i] - ref[i]) / np.linalg.norm(ref[i])
-        worst = np.abs(got[i] - ref[i]).max() / rms
-        assert rel <= ROW_REL_L2 and worst <= ELEM_OF_RMS, (where, i, rel, worst)
-    return ref
+    assert got.shape == Y.shape, (got.shape, Y.shape)
+    h_sq = np.sqrt((H * H) @ (wd * wd).T)                # sqrt(sum_f H_f^2 Wd_if^2)
+    h_abs = np.abs(H) @ np.abs(wd).T                     # sum_f |H_f Wd_if|
+    bound = U_BF16 * np.abs(Y) + LAMBDA * (U_BF16 / np.sqrt(3.0)) * h_sq + SLACK_FP32 * h_abs
+    err = np.abs(got - Y)
+    ratio = err / np.maximum(bound, 1e-300)
+    worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    assert ratio.max() <= 1.0, (where, worst, got[worst], Y[worst], bound[worst])
+    sigma = (U_BF16 / np.sqrt(3.0)) * np.sqrt(h_sq ** 2 + Y ** 2)
+    rms = float(np.sqrt(np.mean((err / np.maximum(sigma, 1e-300)) ** 2)))
+    assert rms <= RMS_UNITS, (where, rms)
+    say(f"  {where}: {Y.size} elements, worst error {ratio.max():.3f} of its bound, "
+        f"RMS {rms:.3f} predicted standard deviations")
+    return Y
 
 
 @pytest.mark.parametrize("rows,D,F", [(300, 256, 512), (1, 64, 8), (77, 128, 1000), (513, 512, 1536)])
@@ -83,16 +111,33 @@ def test_ffn_zero_rows_is_a_no_op():
     assert bool((y == 3.0).all())
 
 
-@pytest.mark.parametrize("model,rows", [("llama8b", 777), ("gemma3", 513)])
-def test_ffn_model_shapes_sampled_rows(model, rows):
+@pytest.mark.parametrize("model,rows", [("llama8b", 128), ("gemma3", 97)])
+def test_ffn_model_shapes_all_rows(model, rows):
+    """LLaMA-3.1-8B (4096 / 14336) and Gemma-3-12B (3840 / 15360) widths:
+    every element of every row against the oracle."""
     D = {"llama8b": 4096, "gemma3": 3840}[model]
     F = synth.FFN_INTERMEDIATE[model]
     wg, wd = host_weights(D, F)
     x = synth.ffn_activations(rows, D)
     ffn = tlb.FFN(D, F)
     y = gpu_ffn(ffn, bits_dev(x), rows, bits_dev(wg), bits_dev(wd))
-    sample = np.array([0, 1, rows // 3, rows // 2, rows - 2, rows - 1])
-    check_rows(y[torch.from_numpy(sample).cuda()], x[sample], wg, wd, model)
+    check_rows(y, x, wg, wd, model)
+
+
+def test_ffn_rows_are_independent_of_their_tile():
+    """The same token rows give bit-identical outputs wherever they sit in the
+    batch (first rows of a tile, last rows, a short last tile): nothing in a
+    row's arithmetic depends on the other rows."""
+    D, F = 512, 1024
+    wg = synth.uniform_bf16_bits(41, 0, 2 * F, D, -4)
+    wd = synth.uniform_bf16_bits(42, 0, D, F, -5)
+    x = synth.uniform_bf16_bits(43, 0, 700, D, 0)
+    ffn = tlb.FFN(D, F)
+    wgd, wdd = bits_dev(wg), bits_dev(wd)
+    full = gpu_ffn(ffn, bits_dev(x), 700, wgd, wdd)
+    for lo, hi in [(0, 37), (250, 262), (511, 700), (699, 700)]:
+        part = gpu_ffn(ffn, bits_dev(x[lo:hi]), hi - lo, wgd, wdd)
+        assert torch.equal(part, full[lo:hi]), (lo, hi)
 
 
 @pytest.mark.timeout(900)
@@ -120,9 +165,8 @@ def test_ffn_on_retained_rows_128k():
     y_kept = gpu_ffn(ffn, xc, K, wgd, wdd)
     y_full = gpu_ffn(ffn, x, T, wgd, wdd)
     idx = cb.index_out[:K].to(torch.int64)
-    a, b = y_kept.float(), y_full[idx].float()
-    rel = (a - b).norm(dim=1) / b.norm(dim=1)
-    assert float(rel.max()) <= ROW_REL_L2, float(rel.max())
+    # a row's output does not depend on where it sits in the stream
+    assert torch.equal(y_kept, y_full[idx])
     # Eq. 8: the full-length state takes the sublayer's output on kept rows only
     full = x.clone()
     run_scatter_back(y_kept.view(torch.int16), cb.index_out, cb.cu_out, 1, T, full.view(torch.int16))
@@ -130,7 +174,7 @@ def test_ffn_on_retained_rows_128k():
     keep_t = dev(mask).bool()
     assert torch.equal(full[~keep_t], x[~keep_t])
     assert torch.equal(full[idx], y_kept)
-    sample = np.sort(rng.choice(np.nonzero(mask)[0], size=6, replace=False))
+    sample = np.sort(rng.choice(np.nonzero(mask)[0], size=64, replace=False))
     xs = np.concatenate([synth.ffn_activations(1, D, row0=int(r)) for r in sample])
-    check_rows(full[torch.from_numpy(sample).cuda()], xs, wg, wd, "128k")
-    say(f"  kept {K}/{T} rows; max row rel diff compacted vs full {float(rel.max()):.2e}")
+    check_rows(full[torch.from_numpy(sample).cuda()], xs, wg, wd, "128k sampled kept rows")
+    say(f"  kept {K}/{T} rows; FFN of the compacted rows bit-identical to the full stream's")

@@ -261,6 +261,18 @@ def _select_variant(mask_at_block_offsets=False, kept_before_forcing=False, roun
     return select
 
 
+def _hidden_variant(swap=False, relu=False):
+    def ffn_hidden(x_bits, w_gate_up_bits):
+        x = U.bf16_bits_to_f64(np.asarray(x_bits))
+        w = U.bf16_bits_to_f64(np.asarray(w_gate_up_bits))
+        F = w.shape[0] // 2
+        g, u = x @ w[:F].T, x @ w[F:].T
+        if swap:
+            g, u = u, g
+        return (np.maximum(g, 0.0) if relu else U.silu(g)) * u
+    return ffn_hidden
+
+
 def _silu_sigmoid(z):
     return 1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64)))
 
@@ -295,6 +307,8 @@ MUTANTS = {
     "ffn_sigmoid_gate": _namespace(ffn_swiglu=_ffn_variant(act="sigmoid")),
     "ffn_no_up_projection": _namespace(ffn_swiglu=_ffn_variant(no_up=True)),
     "silu_is_sigmoid": _namespace(silu=_silu_sigmoid),
+    "ffn_hidden_gate_up_swapped": _namespace(ffn_hidden=_hidden_variant(swap=True)),
+    "ffn_hidden_relu_gate": _namespace(ffn_hidden=_hidden_variant(relu=True)),
     "select_mask_at_block_offsets": _namespace(select=_select_variant(mask_at_block_offsets=True)),
     "select_kept_before_forcing": _namespace(select=_select_variant(kept_before_forcing=True)),
     "select_scores_unrounded": _namespace(select=_select_variant(rounding="none")),

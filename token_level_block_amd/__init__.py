@@ -42,8 +42,8 @@ UP_SCORES_IN = 1
 
 EXPORTED = ("up_max_blocks", "up_select_workspace_bytes", "up_select_blocks", "up_select_blocks_profiled",
             "up_compact_workspace_bytes", "up_compact", "up_scatter_back",
-            "up_update_metadata", "up_slot_mapping", "up_write_kv_cache", "up_ffn_create",
-            "up_ffn_destroy", "up_ffn_workspace_bytes", "up_ffn_forward", "up_status_string")
+            "up_update_metadata", "up_slot_mapping", "up_write_kv_cache",
+            "up_ffn_workspace_bytes", "up_ffn_forward", "up_status_string")
 
 
 class SelectParams(ctypes.Structure):
@@ -92,14 +92,10 @@ _lib.up_slot_mapping.restype = ctypes.c_int
 _lib.up_slot_mapping.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _i32, _i64, _vp, _vp]
 _lib.up_write_kv_cache.restype = ctypes.c_int
 _lib.up_write_kv_cache.argtypes = [_vp, _i64, _vp, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _vp, _i64, _vp]
-_lib.up_ffn_create.restype = ctypes.c_int
-_lib.up_ffn_create.argtypes = [_i32, _i32, ctypes.POINTER(_vp)]
-_lib.up_ffn_destroy.restype = None
-_lib.up_ffn_destroy.argtypes = [_vp]
 _lib.up_ffn_workspace_bytes.restype = _sz
-_lib.up_ffn_workspace_bytes.argtypes = [_vp, _i64]
+_lib.up_ffn_workspace_bytes.argtypes = [_i32, _i32, _i64]
 _lib.up_ffn_forward.restype = ctypes.c_int
-_lib.up_ffn_forward.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.up_ffn_forward.argtypes = [_i32, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.up_status_string.restype = ctypes.c_char_p
 _lib.up_status_string.argtypes = [ctypes.c_int]
 
@@ -235,43 +231,37 @@ def write_kv_cache(key, key_row_stride, value, value_row_stride, row_bytes, slot
     return _check(st, "up_write_kv_cache", raise_on_error)
 
 
+def ffn_workspace_bytes(hidden: int, intermediate: int, rows: int) -> int:
+    return int(_lib.up_ffn_workspace_bytes(hidden, intermediate, rows))
+
+
+def ffn_forward(hidden, intermediate, x, rows, w_gate_up, w_down, y, workspace, workspace_bytes=None,
+                stream=None, raise_on_error=True):
+    """up_ffn_forward: the gated FFN sublayer on `rows` rows (allocation-free)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.up_ffn_forward(hidden, intermediate, _ptr(x), rows, _ptr(w_gate_up), _ptr(w_down), _ptr(y),
+                             _ptr(workspace), workspace_bytes, _stream(stream))
+    return _check(st, "up_ffn_forward", raise_on_error)
+
+
 class FFN:
-    """up_ffn_*: the gated FFN sublayer (hidden D, intermediate F) that runs on
-    the retained rows after a drop.  Holds the library's up_ffn context."""
+    """The gated FFN sublayer (hidden D, intermediate F) that runs on the
+    retained rows after a drop: holds the two widths and forwards to
+    up_ffn_workspace_bytes / up_ffn_forward."""
 
     def __init__(self, hidden: int, intermediate: int):
-        h = _vp()
-        _check(_lib.up_ffn_create(hidden, intermediate, ctypes.byref(h)), "up_ffn_create", True)
-        self.handle = h.value
+        if _lib.up_ffn_workspace_bytes(hidden, intermediate, 0) == 0:
+            raise UniPrefillError(UP_ERR_PARAM, "FFN widths")
         self.hidden, self.intermediate = hidden, intermediate
 
     def workspace_bytes(self, rows: int) -> int:
-        return int(_lib.up_ffn_workspace_bytes(self.handle, rows))
+        return ffn_workspace_bytes(self.hidden, self.intermediate, rows)
 
     def forward(self, x, rows, w_gate_up, w_down, y, workspace, workspace_bytes=None, stream=None,
                 raise_on_error=True):
-        if workspace_bytes is None:
-            workspace_bytes = workspace.numel() * workspace.element_size()
-        st = _lib.up_ffn_forward(self.handle, _ptr(x), rows, _ptr(w_gate_up), _ptr(w_down), _ptr(y),
-                                 _ptr(workspace), workspace_bytes, _stream(stream))
-        return _check(st, "up_ffn_forward", raise_on_error)
+        return ffn_forward(self.hidden, self.intermediate, x, rows, w_gate_up, w_down, y, workspace,
+                           workspace_bytes, stream, raise_on_error)
 
     def close(self):
-        if self.handle:
-            _lib.up_ffn_destroy(self.handle)
-            self.handle = None
-
-    def __del__(self):
-        try:
-            self.close()
-        except Exception:
-            pass
-
-
-def ffn_create_status(hidden: int, intermediate: int) -> int:
-    """Status of up_ffn_create alone (argument checks), destroying any context made."""
-    h = _vp()
-    st = _lib.up_ffn_create(hidden, intermediate, ctypes.byref(h))
-    if h.value:
-        _lib.up_ffn_destroy(h.value)
-    return st
+        pass

@@ -6,8 +6,8 @@
 is being rebuilt).
 
 Every .hip file under csrc/ is compiled to an object in _build/ and linked
-into token_level_block_amd/libuniprefill.so (with hipBLASLt, which the FFN
-sublayer's two projections use).  peaks/peaks.hip (reference
+into token_level_block_amd/libuniprefill.so (HIP runtime only: every kernel,
+the FFN sublayer's GEMMs included, is in csrc/).  peaks/peaks.hip (reference
 MFMA and copy rates, loaded only by the benchmark) becomes libuppeaks.so.
 Packed fp32 instructions are disabled for all device code.
 """
@@ -73,7 +73,7 @@ def build(verbose: bool = True) -> str:
         if warn.strip() and verbose:
             print(warn, file=sys.stderr)
     objs = [o for o, _ in results]
-    _link(hipcc, objs[:-1], LIB, ["-L/opt/rocm/lib", "-lhipblaslt"])
+    _link(hipcc, objs[:-1], LIB)
     _link(hipcc, objs[-1:], PEAKS_LIB)
     if verbose:
         print(f"built {LIB} and {PEAKS_LIB}")
