@@ -9,8 +9,9 @@
  *   - All buffers are caller-owned DEVICE memory unless marked (host).
  *   - Every call only enqueues work on `stream` (a hipStream_t; 0 is the null
  *     stream).  No call allocates, frees or synchronises, and the library
- *     keeps no global state: calls are re-entrant and thread-safe on disjoint
- *     buffers.
+ *     keeps no global state (the one exception is the per-GPU scratch of
+ *     up_compact_noalloc, below): calls are re-entrant and thread-safe on
+ *     disjoint buffers.
  *   - Arguments are validated on the host before anything is enqueued.  A bad
  *     argument returns a negative up_status and changes nothing.  A failed
  *     launch returns UP_ERR_HIP.  Faults inside kernels surface at the
@@ -144,6 +145,28 @@ up_status up_compact(const uint8_t* keep_mask, const int32_t* cu_seqlens, int32_
                      const void* const* src, void* const* dst, const int64_t* row_bytes,
                      const int32_t* index_in, int32_t* index_out, int32_t* cu_seqlens_out,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * up_compact_noalloc - up_compact for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, work, results and validation as
+ * up_compact, without the workspace: the library uses a scratch array of
+ * 16 MiB in device memory that exists once per GPU from the first call on that
+ * GPU (the GPU of `stream`) until the process ends.  The call allocates
+ * nothing; it accepts streams of at most UP_COMPACT_NOALLOC_MAX_TOKENS tokens
+ * (max_tokens above it returns UP_ERR_WORKSPACE before any work) and returns
+ * UP_ERR_HIP if the scratch cannot be located on that GPU.  Every call on one
+ * GPU shares its scratch: calls whose work overlaps on the same GPU (two
+ * streams, or two host threads, without ordering between them) race and give
+ * undefined results; calls ordered on one stream are safe.  The scratch keeps
+ * the last call's contents, and nothing in it needs to start at zero.
+ */
+#define UP_COMPACT_NOALLOC_MAX_TOKENS 4000000
+up_status up_compact_noalloc(const uint8_t* keep_mask, const int32_t* cu_seqlens, int32_t num_reqs,
+                             int64_t max_tokens, int32_t num_buffers,
+                             const void* const* src, void* const* dst, const int64_t* row_bytes,
+                             const int32_t* index_in, int32_t* index_out, int32_t* cu_seqlens_out,
+                             hipStream_t stream);
 
 /*
  * up_scatter_back - carry-forward of UniPrefill Sec. 3.4 Eq. 8: for

@@ -146,6 +146,25 @@ def test_compact_rejects():
     assert call_compact(wsb=tlb.compact_workspace_bytes(2, 1000) - 1) == tlb.UP_ERR_WORKSPACE
 
 
+def test_compact_noalloc_rejects_before_any_hip_work():
+    """Same validation as up_compact, and streams past the scratch's maximum
+    rejected up front (the scratch is never located for a rejected call)."""
+    lib = tlb._lib
+    vp = ctypes.c_void_p
+    src = (vp * 1)(FAKE)
+    dst = (vp * 1)(FAKE + 4096)
+    rb = (ctypes.c_int64 * 1)(16)
+    call = lambda mask, cu, R, T, n=1, rbx=rb: lib.up_compact_noalloc(mask, cu, R, T, n, src, dst, rbx, None, FAKE,
+                                                                     FAKE, None)
+    assert tlb.COMPACT_NOALLOC_MAX_TOKENS == 4000000
+    assert call(FAKE, FAKE, 1, tlb.COMPACT_NOALLOC_MAX_TOKENS + 1) == tlb.UP_ERR_WORKSPACE
+    assert call(FAKE, FAKE, -1, 100) == tlb.UP_ERR_SHAPE
+    assert call(None, FAKE, 1, 100) == tlb.UP_ERR_NULL
+    assert call(FAKE_MIS, FAKE, 1, 100) == tlb.UP_ERR_ALIGN
+    assert call(FAKE, FAKE, 1, 100, n=9) == tlb.UP_ERR_PARAM
+    assert call(FAKE, FAKE, 1, 100, rbx=(ctypes.c_int64 * 1)(6)) == tlb.UP_ERR_PARAM
+
+
 def test_scatter_and_metadata_reject():
     sb = lambda **kw: tlb.scatter_back(kw.get("c", FAKE), kw.get("rb", 16), kw.get("im", FAKE), FAKE,
                                        kw.get("R", 1), 10, kw.get("full", FAKE), kw.get("fr", 10),

@@ -41,7 +41,7 @@ UP_ERR_HIP = -6
 UP_SCORES_IN = 1
 
 EXPORTED = ("up_max_blocks", "up_select_workspace_bytes", "up_select_blocks", "up_select_blocks_profiled",
-            "up_compact_workspace_bytes", "up_compact", "up_scatter_back",
+            "up_compact_workspace_bytes", "up_compact", "up_compact_noalloc", "up_scatter_back",
             "up_update_metadata", "up_slot_mapping", "up_write_kv_cache",
             "up_ffn_workspace_bytes", "up_ffn_forward", "up_status_string")
 
@@ -84,6 +84,9 @@ _lib.up_compact_workspace_bytes.argtypes = [_i32, _i64]
 _lib.up_compact.restype = ctypes.c_int
 _lib.up_compact.argtypes = [_vp, _vp, _i32, _i64, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                             ctypes.POINTER(_i64), _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.up_compact_noalloc.restype = ctypes.c_int
+_lib.up_compact_noalloc.argtypes = [_vp, _vp, _i32, _i64, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                    ctypes.POINTER(_i64), _vp, _vp, _vp, _vp]
 _lib.up_scatter_back.restype = ctypes.c_int
 _lib.up_scatter_back.argtypes = [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _vp]
 _lib.up_update_metadata.restype = ctypes.c_int
@@ -192,6 +195,24 @@ def compact(keep_mask, cu_seqlens, num_reqs, max_tokens, src, dst, row_bytes, in
                          rb_arr, _ptr(index_in), _ptr(index_out), _ptr(cu_seqlens_out), _ptr(workspace),
                          workspace_bytes, _stream(stream))
     return _check(st, "up_compact", raise_on_error)
+
+
+COMPACT_NOALLOC_MAX_TOKENS = 4000000   # UP_COMPACT_NOALLOC_MAX_TOKENS
+
+
+def compact_noalloc(keep_mask, cu_seqlens, num_reqs, max_tokens, src, dst, row_bytes, index_in, index_out,
+                    cu_seqlens_out, stream=None, raise_on_error=True):
+    """up_compact_noalloc: up_compact without a workspace (the library's
+    per-GPU scratch; at most COMPACT_NOALLOC_MAX_TOKENS tokens)."""
+    nb = len(src)
+    if len(dst) != nb or len(row_bytes) != nb:
+        raise ValueError("src, dst and row_bytes must have one entry per buffer")
+    src_arr = (_vp * max(nb, 1))(*[_ptr(x) for x in src])
+    dst_arr = (_vp * max(nb, 1))(*[_ptr(x) for x in dst])
+    rb_arr = (_i64 * max(nb, 1))(*[int(x) for x in row_bytes])
+    st = _lib.up_compact_noalloc(_ptr(keep_mask), _ptr(cu_seqlens), num_reqs, max_tokens, nb, src_arr, dst_arr,
+                                 rb_arr, _ptr(index_in), _ptr(index_out), _ptr(cu_seqlens_out), _stream(stream))
+    return _check(st, "up_compact_noalloc", raise_on_error)
 
 
 def scatter_back(compacted, row_bytes, index_map, cu_seqlens_out, num_reqs, max_tokens, full,

@@ -3,6 +3,8 @@
 // argument leaves all buffers untouched.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/uniprefill.h"
 #include "../../include/uniprefill_prof.h"
 #include "common.h"
@@ -78,7 +80,87 @@ up_status plan_select(const up_select_params* prm, int32_t R, int64_t max_tokens
   return UP_OK;
 }
 
+// Every check of up_compact except the workspace; fills everything in `a`
+// but the workspace pointers.  No side effects.
+up_status prepare_compact(const uint8_t* keep_mask, const int32_t* cu_seqlens, int32_t num_reqs,
+                          int64_t max_tokens, int32_t num_buffers, const void* const* src, void* const* dst,
+                          const int64_t* row_bytes, const int32_t* index_in, int32_t* index_out,
+                          int32_t* cu_seqlens_out, up::CompactArgs* a) {
+  if (num_reqs < 0 || max_tokens < 0 || max_tokens > INT32_MAX) return UP_ERR_SHAPE;
+  if (num_buffers < 0 || num_buffers > up::kMaxCompactBuffers) return UP_ERR_PARAM;
+  if (keep_mask == nullptr || cu_seqlens == nullptr || index_out == nullptr || cu_seqlens_out == nullptr)
+    return UP_ERR_NULL;
+  if (num_buffers > 0 && (src == nullptr || dst == nullptr || row_bytes == nullptr)) return UP_ERR_NULL;
+  a->bufs.nbuf = num_buffers;
+  for (int b = 0; b < num_buffers; ++b) {
+    if (src[b] == nullptr || dst[b] == nullptr) return UP_ERR_NULL;
+    if (row_bytes[b] <= 0 || row_bytes[b] % 4 != 0) return UP_ERR_PARAM;
+    if (!aligned(src[b], 4) || !aligned(dst[b], 4)) return UP_ERR_ALIGN;
+    a->bufs.src[b] = static_cast<const uint8_t*>(src[b]);
+    a->bufs.dst[b] = static_cast<uint8_t*>(dst[b]);
+    a->bufs.row_bytes[b] = row_bytes[b];
+    a->bufs.vec16[b] = (row_bytes[b] % 16 == 0 && aligned(src[b], 16) && aligned(dst[b], 16)) ? 1 : 0;
+  }
+  if (!aligned(keep_mask, 16)) return UP_ERR_ALIGN;
+  a->num_count_tiles = (max_tokens + up::kCountTile - 1) / up::kCountTile;
+  a->mask = keep_mask;
+  a->cu_in = cu_seqlens;
+  a->R = num_reqs;
+  a->max_tokens = max_tokens;
+  a->index_in = index_in;
+  a->index_out = index_out;
+  a->cu_out = cu_seqlens_out;
+  return UP_OK;
+}
+
+// compaction workspace layout (up_compact_workspace_bytes): per-4096-token
+// counts, then the stream position of each kept row
+void place_compact_workspace(up::CompactArgs* a, uint8_t* ws) {
+  const int64_t ntiles = a->num_count_tiles;
+  a->tile_count = reinterpret_cast<int32_t*>(ws);
+  a->src_pos = reinterpret_cast<int32_t*>(ws + align_up(sizeof(int32_t) * (size_t)(ntiles > 0 ? ntiles : 1)));
+}
+
 }  // namespace
+
+// Scratch of up_compact_noalloc: one copy per GPU, alive until the process
+// ends.  Host code never uses this name as an address (on the host it is a
+// stand-in, not device memory): it uses the per-device address that
+// hipGetSymbolAddress returns for it.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices];   // address of `scratch` on each device, null until looked up
+
+// The device `stream` runs on, its copy of `scratch` (looked up once per
+// device, with that device current).
+up_status scratch_of_stream_device(hipStream_t stream, uint8_t** out) {
+  int dev = -1;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return UP_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return UP_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return UP_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return UP_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return UP_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return UP_OK;
+}
+
+}  // namespace
+
+static_assert(((UP_COMPACT_NOALLOC_MAX_TOKENS + 4095) / 4096 * 4 + 255) / 256 * 256 +
+                      (size_t)UP_COMPACT_NOALLOC_MAX_TOKENS * 4 <= kNoAllocScratchBytes,
+              "the static scratch holds the compaction workspace of its largest stream");
 
 extern "C" {
 
@@ -261,39 +343,30 @@ up_status up_compact(const uint8_t* keep_mask, const int32_t* cu_seqlens, int32_
                      void* const* dst, const int64_t* row_bytes, const int32_t* index_in,
                      int32_t* index_out, int32_t* cu_seqlens_out, void* workspace,
                      size_t workspace_bytes, hipStream_t stream) {
-  if (num_reqs < 0 || max_tokens < 0 || max_tokens > INT32_MAX) return UP_ERR_SHAPE;
-  if (num_buffers < 0 || num_buffers > up::kMaxCompactBuffers) return UP_ERR_PARAM;
-  if (keep_mask == nullptr || cu_seqlens == nullptr || index_out == nullptr ||
-      cu_seqlens_out == nullptr || workspace == nullptr)
-    return UP_ERR_NULL;
-  if (num_buffers > 0 && (src == nullptr || dst == nullptr || row_bytes == nullptr)) return UP_ERR_NULL;
   up::CompactArgs a;
-  a.bufs.nbuf = num_buffers;
-  for (int b = 0; b < num_buffers; ++b) {
-    if (src[b] == nullptr || dst[b] == nullptr) return UP_ERR_NULL;
-    if (row_bytes[b] <= 0 || row_bytes[b] % 4 != 0) return UP_ERR_PARAM;
-    if (!aligned(src[b], 4) || !aligned(dst[b], 4)) return UP_ERR_ALIGN;
-    a.bufs.src[b] = static_cast<const uint8_t*>(src[b]);
-    a.bufs.dst[b] = static_cast<uint8_t*>(dst[b]);
-    a.bufs.row_bytes[b] = row_bytes[b];
-    a.bufs.vec16[b] = (row_bytes[b] % 16 == 0 && aligned(src[b], 16) && aligned(dst[b], 16)) ? 1 : 0;
-  }
-  if (!aligned(keep_mask, 16) || !aligned(workspace, kAlign)) return UP_ERR_ALIGN;
-  const size_t need = up_compact_workspace_bytes(num_reqs, max_tokens);
-  if (workspace_bytes < need) return UP_ERR_WORKSPACE;
+  const up_status st = prepare_compact(keep_mask, cu_seqlens, num_reqs, max_tokens, num_buffers, src, dst,
+                                       row_bytes, index_in, index_out, cu_seqlens_out, &a);
+  if (st != UP_OK) return st;
+  if (workspace == nullptr) return UP_ERR_NULL;
+  if (!aligned(workspace, kAlign)) return UP_ERR_ALIGN;
+  if (workspace_bytes < up_compact_workspace_bytes(num_reqs, max_tokens)) return UP_ERR_WORKSPACE;
+  place_compact_workspace(&a, static_cast<uint8_t*>(workspace));
+  if (up::launch_compact(a, stream) != hipSuccess) return UP_ERR_HIP;
+  return UP_OK;
+}
 
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const int64_t ntiles = (max_tokens + up::kCountTile - 1) / up::kCountTile;
-  a.tile_count = reinterpret_cast<int32_t*>(ws);
-  a.src_pos = reinterpret_cast<int32_t*>(ws + align_up(sizeof(int32_t) * (size_t)(ntiles > 0 ? ntiles : 1)));
-  a.num_count_tiles = ntiles;
-  a.mask = keep_mask;
-  a.cu_in = cu_seqlens;
-  a.R = num_reqs;
-  a.max_tokens = max_tokens;
-  a.index_in = index_in;
-  a.index_out = index_out;
-  a.cu_out = cu_seqlens_out;
+up_status up_compact_noalloc(const uint8_t* keep_mask, const int32_t* cu_seqlens, int32_t num_reqs,
+                             int64_t max_tokens, int32_t num_buffers, const void* const* src,
+                             void* const* dst, const int64_t* row_bytes, const int32_t* index_in,
+                             int32_t* index_out, int32_t* cu_seqlens_out, hipStream_t stream) {
+  up::CompactArgs a;
+  const up_status st = prepare_compact(keep_mask, cu_seqlens, num_reqs, max_tokens, num_buffers, src, dst,
+                                       row_bytes, index_in, index_out, cu_seqlens_out, &a);
+  if (st != UP_OK) return st;
+  if (max_tokens > UP_COMPACT_NOALLOC_MAX_TOKENS) return UP_ERR_WORKSPACE;
+  uint8_t* ws = nullptr;
+  if (scratch_of_stream_device(stream, &ws) != UP_OK) return UP_ERR_HIP;
+  place_compact_workspace(&a, ws);
   if (up::launch_compact(a, stream) != hipSuccess) return UP_ERR_HIP;
   return UP_OK;
 }
