@@ -51,7 +51,9 @@ STRUCT_BLOCK = 64    # granularity of the generator's hot/cold structure
 # Calibrated generator constants (see tests/golden/calibrate_generator.py,
 # which bisects them against the oracle's keep ratio at p = 0.99).
 POWERLAW_C = 1.4590  # keeps 40.1% of the 2048 blocks of the 128K request at p = 0.99
-HOT_LAMBDA_VARLEN = 8.0
+# hot-block alignment of each request of the varlen batch: the requests keep
+# 9.4%, 34.4%, 60.2% and 100% of their tokens (the last has only hot blocks)
+HOT_LAMBDA_VARLEN = (8.0, 6.9462, 6.2224, 8.0)
 
 LLAMA_8B = dict(hq=32, hkv=8, d=128, hidden=4096)
 QWEN_NEXT = dict(hq=16, hkv=2, d=256, hidden=2048)
@@ -203,6 +205,19 @@ def make_qk(wl: Workload, workers: int | None = None):
     return cu, q, k
 
 
+def make_request_qk(wl: Workload, r: int):
+    """Request r of make_qk(wl) on its own: (q uint16 [N_r, Hq, d], k uint16
+    [N_r, Hkv, d]), bit-identical to rows cu[r] .. cu[r+1]-1 of make_qk's
+    arrays (each request and KV head draws from its own stream)."""
+    N = int(wl.lengths[r])
+    q = np.zeros((N, wl.hq, wl.d), dtype=np.uint16)
+    k = np.zeros((N, wl.hkv, wl.d), dtype=np.uint16)
+    lam = token_lambdas(wl, r)
+    for j in range(wl.hkv):
+        _fill_request_head(wl, r, j, 0, lam, q, k)
+    return q, k
+
+
 def random_scores(rng: np.random.Generator, nb: int, kind: str = "lognormal") -> np.ndarray:
     """Non-negative fp32 block-score vectors for feeding selection directly."""
     if kind == "lognormal":
@@ -330,11 +345,13 @@ def llama_4k(seed: int = 0) -> Workload:
                     structures=(RequestStructure("hot", hot=6, hot_lambda=2.0),), **LLAMA_8B)
 
 
-def llama_varlen4(seed: int = 1, hot_lambda: float | None = None) -> Workload:
+def llama_varlen4(seed: int = 1, hot_lambda=None) -> Workload:
+    """hot_lambda: one alignment for all four requests, or one per request."""
     lam = HOT_LAMBDA_VARLEN if hot_lambda is None else hot_lambda
+    lams = tuple(lam) if isinstance(lam, (tuple, list)) else (float(lam),) * 4
     hots = (2, 8, 20, 64)
     return Workload("llama8b_varlen4", (4096, 8192, 16384, 2048), seed=seed,
-                    structures=tuple(RequestStructure("hot", hot=h, hot_lambda=lam) for h in hots),
+                    structures=tuple(RequestStructure("hot", hot=h, hot_lambda=l) for h, l in zip(hots, lams)),
                     **LLAMA_8B)
 
 
