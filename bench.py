@@ -287,6 +287,74 @@ def run_sweep(args, ev, stream):
     print(json.dumps({"sweep": records}), flush=True)
 
 
+def select_compact_hbm(wl, m):
+    """The select + compact HBM figure of one measured step: algorithmic bytes
+    (kept hidden rows and positions read and written, index map, token mask,
+    block scores and flags) over the time of the kernels that move them (select
+    and compact without the score GEMM, whose time is the MFMA roofline's)."""
+    kept, T, row_bytes = m["kept"], m["T"], wl.hidden * 2
+    nbytes = 2 * kept * row_bytes + 2 * 4 * kept + 4 * kept + T + 5 * m["nblocks"]
+    ms = m["select_ms"] - m["score_ms"] + m["compact_ms"]
+    return nbytes, ms, nbytes / (ms * 1e-3) / 1e9
+
+
+def config_record(label, wl, m, note=None):
+    """One record of the default line's `configs` array."""
+    T = m["T"]
+    flops = sum(2.0 * min(wl.n, L) * wl.hq * wl.d * L for L in wl.lengths)
+    score_tflops = flops / (m["score_ms"] * 1e-3) / 1e12
+    nbytes, sc_ms, sc_gbs = select_compact_hbm(wl, m)
+    rec = {"config": label, "workload": wl.name, "requests": m["R"], "tokens": T,
+           "num_heads_q": wl.hq, "num_heads_kv": wl.hkv, "head_dim": wl.d, "hidden": wl.hidden,
+           "G": wl.G, "A": wl.A, "n": wl.n, "p": wl.p,
+           "ms_per_step": m["ms_per_step"], "launch": "hip_graph" if m["ms_graph"] is not None else "eager",
+           "tokens_per_s": T / (m["ms_per_step"] * 1e-3),
+           "ms_per_step_mall_flushed": m["ms_flushed"],
+           "tokens_per_s_mall_flushed": T / (m["ms_flushed"] * 1e-3),
+           "breakdown_ms": {"select": m["select_ms"], "score_kernel": m["score_ms"], "compact": m["compact_ms"],
+                            "metadata": m["meta_ms"], "scatter_back": m["scatter_ms"]},
+           "score_tflops": score_tflops, "score_frac": score_tflops / PEAK_BF16_TFLOPS,
+           "select_compact_gbs": sc_gbs, "select_compact_frac": sc_gbs / PEAK_HBM_GBS,
+           "select_compact_bytes": nbytes,
+           "keep_ratio": m["kept"] / T,
+           "keep_ratio_per_request": [round(k / L, 4) if L else None for k, L in zip(m["kept_per_req"], wl.lengths)]}
+    if note:
+        rec["note"] = note
+    return rec
+
+
+def run_configs(steps, warmup, ev, stream):
+    """Every workload of the benchmark's configuration list except the
+    headline's 128K request: the 4K request, the 4-request varlen batch, the
+    Qwen3-Next- and Gemma-3-shaped 64K layers at G = 32 / 64 / 128 (and Gemma
+    at p = 0.98, the paper's Gemma setting), and both drop layers of the
+    16 x 128K serving batch."""
+    import torch
+    import synth
+    items = [("0", synth.llama_4k(), None), ("1", synth.llama_varlen4(), None)]
+    items += [(f"3a_G{G}", synth.hybrid_64k("qwen_next", G), None) for G in (32, 64, 128)]
+    items += [(f"3b_G{G}", synth.hybrid_64k("gemma3", G), None) for G in (32, 64, 128)]
+    items += [("3b_G64_p0.98", synth.hybrid_64k("gemma3", 64, p=0.98), None)]
+    items += [("4_layer0", synth.serving_16x128k(layer=0), None),
+              ("4_layer1", synth.serving_16x128k(lengths=synth.serving_16x128k_layer1_lengths(), layer=1),
+               "second selection on a compacted stream: the lengths are the tokens of the first layer's "
+               "planted hot blocks plus its sink and window blocks (the GPU's own layer-0 kept counts "
+               "drive it in the parity test)")]
+    out = []
+    for label, wl, note in items:
+        t0 = time.perf_counter()
+        m = measure_step(wl, steps, warmup, ev, stream)
+        rec = config_record(label, wl, m, note)
+        rec["setup_and_timing_s"] = round(time.perf_counter() - t0, 1)
+        log(f"[configs] {label} {wl.name}: {rec['ms_per_step']:.3f} ms/step ({rec['ms_per_step_mall_flushed']:.3f} "
+            f"flushed), score {rec['score_tflops']:.0f} TFLOP/s ({rec['score_frac']:.3f}), select+compact "
+            f"{rec['select_compact_gbs']:.0f} GB/s ({rec['select_compact_frac']:.3f}), keep {rec['keep_ratio']:.3f}")
+        out.append(rec)
+        del m
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_model():
     """The host CPU's model name (first /proc/cpuinfo entry), or None."""
     try:
@@ -442,6 +510,23 @@ def measure_step(wl, steps, warmup, ev, stream, pipelined=False):
         log(f"[bench] {graph_note}")
     ms_per_step = ms_graph if ms_graph is not None else ms_eager
 
+    # the same step with the 256 MB MALL flushed before each one: a 512 MB
+    # read (no dirty lines left to write back inside the timed step), then the
+    # step between two events; the median over K steps
+    flush = torch.ones(1 << 27, dtype=torch.int32, device="cuda")
+    sink = torch.empty((), dtype=torch.int64, device="cuda")
+    run_one = graph.replay if ms_graph is not None else (lambda: step(stream))
+    fmarks = [(ev.new(), ev.new()) for _ in range(args.steps)]
+    for a, b in fmarks:
+        torch.sum(flush, dim=0, dtype=torch.int64, out=sink)
+        ev.record(a, stream)
+        run_one()
+        ev.record(b, stream)
+    torch.cuda.synchronize()
+    flushed = sorted(ev.ms(a, b) for a, b in fmarks)
+    ms_flushed = flushed[len(flushed) // 2]
+    del flush, sink
+
     def mean(a, b):
         return sum(ev.ms(m[a], m[b]) for m in marks) / len(marks)
 
@@ -455,7 +540,10 @@ def measure_step(wl, steps, warmup, ev, stream, pipelined=False):
     if two is not None:
         two["ms_one_stream"] = ms_per_step
         two["speedup"] = ms_per_step / two["ms_per_batch"]
+    kept_per_req = sel.kept[:R].cpu().tolist()
+    nblocks = int(sel.block_offsets[R].item())
     return dict(wl=wl, T=T, R=R, kept=kept, cu=cu, q=q, k=k, cu_d=cu_d, sel=sel, cb=cb, nwords=nwords,
+                kept_per_req=kept_per_req, nblocks=nblocks, ms_flushed=ms_flushed,
                 ms_eager=ms_eager, ms_graph=ms_graph, graph_note=graph_note, ms_per_step=ms_per_step,
                 score_ms=score_ms, select_ms=select_ms, compact_ms=compact_ms, meta_ms=meta_ms,
                 scatter_ms=scatter_ms, two=two, release=lambda: None)
@@ -535,6 +623,8 @@ def main():
     ap.add_argument("--step-only", action="store_true",
                     help="time the step only: skip the next-row extras (Eq. 16 slots and KV write, the FFN) "
                          "and the measured peaks (for short profiled runs)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration records (configs 0, 1, 3, 4) of the default line")
     ap.add_argument("--sweep", action="store_true",
                     help="time the step on every workload shape (4K to 16 x 128K) instead of the benchmark line")
     ap.add_argument("--two-in-flight", action="store_true",
@@ -601,10 +691,7 @@ def main():
     # (select and compact without the score GEMM, whose K reads and time are
     # counted under the MFMA roofline); and, for the whole select + compact, the
     # same bytes plus the score GEMM's K and window-query reads over the whole time
-    nblocks = int(sel.block_offsets[R].item())
-    sc_bytes = 2 * kept * row_bytes + 2 * 4 * kept + 4 * kept + T + 5 * nblocks
-    sc_ms = select_ms - score_ms + compact_ms
-    sc_gbs = sc_bytes / (sc_ms * 1e-3) / 1e9
+    sc_bytes, sc_ms, sc_gbs = select_compact_hbm(wl, m)
     qk_bytes = 2 * T * wl.hkv * wl.d + 2 * R * min(wl.n, T) * wl.hq * wl.d
     all_gbs = (sc_bytes + qk_bytes) / ((select_ms + compact_ms) * 1e-3) / 1e9
     torch.cuda.empty_cache()
@@ -624,6 +711,9 @@ def main():
         kv["frac"] = kv["write_gbs"] / PEAK_HBM_GBS
         kv["frac_measured"] = kv["write_gbs"] / copy_peak
         log(f"[bench] measured peaks: bf16 MFMA {mfma_peak:.0f} TFLOP/s (random operands), copy {copy_peak:.0f} GB/s")
+    configs = None
+    if not (args.step_only or args.no_configs):
+        configs = run_configs(args.steps, args.warmup, ev, stream)
     ev.close()
 
     cpu = None
@@ -686,6 +776,8 @@ def main():
                            "how": "libuppeaks: random-operand 32x32x16 bf16 MFMA loop at 2 waves/SIMD; "
                                   "1 GiB streaming copy, one 16-byte unit per thread in one pass, "
                                   "read + write bytes"},
+        "ms_per_step_mall_flushed": m["ms_flushed"],
+        "configs": configs,
         "launch": "hip_graph" if ms_graph is not None else f"eager ({graph_note})",
         "ms_per_step_eager": ms_eager,
         "ms_per_step_graph": ms_graph,
