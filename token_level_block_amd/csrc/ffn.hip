@@ -13,10 +13,12 @@
 //   2. down: i over the D rows of Wd, j over the tokens, K = F; y as bf16.
 // A workgroup computes a 256 (weight rows) x 256 (tokens) tile with
 // v_mfma_f32_32x32x16_bf16: four waves of 128 x 128, each holding 4 x 4
-// accumulator tiles.  Operands stream through a two-stage LDS ring with
-// gfx950's direct global-to-LDS 16-byte loads, 64 K-elements per stage, in
-// 128-byte rows whose 16-byte pieces are XOR-swizzled by (row / 2) & 7, so
-// the 16 lanes of each pass of a fragment read hit 16 different bank groups.
+// accumulator tiles.  Operands stream through a four-stage LDS ring with
+// gfx950's direct global-to-LDS 16-byte loads, 32 K-elements per stage, each
+// stage's loads issued three stages before it is consumed (the loads come from
+// L2 or further: one stage of lead left the waves waiting on them).  Rows are
+// 64 bytes; their 16-byte pieces are XOR-swizzled by (row / 4) & 3, so the 16
+// lanes of each pass of a fragment read hit 16 different bank groups.
 // In the gate/up launch the workgroup's 256 weight rows are 64 gate rows, the
 // 64 up rows of the same channels, then the next 64 of each: a wave's first
 // two accumulator rows of tiles are gate and its last two the matching up
@@ -38,8 +40,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kFfnThreads = 256;          // four waves
 constexpr int kTileI = 256;               // weight rows per workgroup
 constexpr int kTileJ = 256;               // tokens per workgroup
-constexpr int kBK = 64;                   // K elements per stage (128-byte rows)
-constexpr int kStageBytes = (kTileI + kTileJ) * kBK * 2;   // 64 KB
+constexpr int kBK = 32;                   // K elements per stage (64-byte rows)
+constexpr int kStages = 4;                // LDS ring depth; loads run kStages - 1 stages ahead
+constexpr int kRowBytes = kBK * 2;
+constexpr int kStageBytes = (kTileI + kTileJ) * kRowBytes;   // 32 KB
+constexpr int kLoadsPerStage = kStageBytes / 4 / 1024;       // 1 KB wave loads per wave per stage (8)
 constexpr int kGroupJ = 8;                // token panels walked together
 
 __device__ __attribute__((aligned(16))) const uint32_t kZeroPiece[4] = {0u, 0u, 0u, 0u};
@@ -61,9 +66,22 @@ __device__ __forceinline__ float silu_f32(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// s_waitcnt vmcnt(n) with the other counters left free (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// a pointer in the LDS address space, as the direct-to-LDS loads take it (cast
+// at the call: a helper, or a lambda, that returns one loses the kernel's
+// host-side launch stub)
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
 template <bool kGateUp>
 __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wi = wid >> 1, wj = wid & 1;
@@ -82,46 +100,64 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
 
   const int64_t K = a.K;
   const int64_t n_w = kGateUp ? 2 * a.F : a.n_out;   // weight rows
-  // weight row of tile row r
-  auto wrow = [&](int r) -> int64_t {
-    int64_t i;
-    if (kGateUp) {
-      // [gate 64 | up 64 | gate 64 | up 64] of channels f0 .. f0 + 127
-      const int64_t f = (int64_t)ti * 128 + (r >> 7) * 64 + (r & 63);
-      i = ((r >> 6) & 1) ? a.F + min(f, a.F - 1) : min(f, a.F - 1);
-    } else {
-      i = min((int64_t)ti * kTileI + r, n_w - 1);
-    }
-    return i;
-  };
 
-  // this lane's loads: wave chunk c (0..7) of the weight tile and of the
-  // token tile covers 8 rows; lane L writes LDS row 8c' + L/8, slot L % 8 and
-  // reads global piece slot ^ ((row / 2) & 7)
-  const uint16_t* wptr[8];
-  const uint16_t* xptr[8];
-  const int slot = lane & 7;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int r = (wid * 8 + c) * 8 + (lane >> 3);
-    const int p = slot ^ ((r >> 1) & 7);
-    wptr[c] = a.w + wrow(r) * K + p * 8;
-    const int64_t j = min((int64_t)tj * kTileJ + r, a.rows - 1);
-    xptr[c] = a.x + j * K + p * 8;
+  // this wave's loads: chunk c (0..3) of its 64 weight rows and of its 64
+  // token rows covers 16 rows, tile row r = 16 (4 wid + c) + L / 4 for lane L,
+  // which fills LDS slot L % 4 of row r with global piece (L % 4) ^ ((r / 4) & 3)
+  // = (L % 4) ^ ((L / 16) & 3).  Rows past the end are clamped.  Each wave
+  // addresses its rows from a uniform first-row pointer plus a fixed 32-bit
+  // lane offset (< 64 K 2 + 64 bytes), so a stage's loads need no vector
+  // arithmetic.
+  // In the gate/up launch tile rows [gate 64 | up 64 | gate 64 | up 64] are the
+  // channels ti*128 + 0..127: wave wid holds gate (wid even) or up (wid odd)
+  // rows of channels ti*128 + (wid / 2)*64 + 0..63.
+  constexpr int kChunks = kLoadsPerStage / 2;
+  const int piece = (lane & 3) ^ ((lane >> 4) & 3);
+  int64_t w_first, w0, w_last;   // first weight row of the wave, unclamped first, last valid
+  if (kGateUp) {
+    const int64_t f0 = (int64_t)ti * 128 + (wid >> 1) * 64;
+    w0 = f0;
+    w_last = a.F - 1;
+    w_first = (wid & 1) ? a.F : 0;   // gate or up half
+  } else {
+    w0 = (int64_t)ti * kTileI + wid * 64;
+    w_last = n_w - 1;
+    w_first = 0;
   }
-  auto load_stage = [&](int64_t kb, int buf) {
-    uint8_t* sbase = smem + buf * kStageBytes;
-    const bool full = kb + kBK <= K;
+  const int64_t wb = min(w0, w_last);
+  const int64_t j0 = (int64_t)tj * kTileJ + wid * 64;
+  const int64_t jb = min(j0, a.rows - 1);
+  const uint8_t* wave_w = reinterpret_cast<const uint8_t*>(a.w + (w_first + wb) * K);
+  const uint8_t* wave_x = reinterpret_cast<const uint8_t*>(a.x + jb * K);
+  uint32_t w_off[kChunks], x_off[kChunks];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int r = (wid * 8 + c) * 8 + (lane >> 3);
-      const int64_t kp = kb + (int64_t)((slot ^ ((r >> 1) & 7)) * 8);   // first K of the piece
-      const void* gw = (full || kp < K) ? (const void*)(wptr[c] + kb) : (const void*)kZeroPiece;
-      const void* gx = (full || kp < K) ? (const void*)(xptr[c] + kb) : (const void*)kZeroPiece;
-      __builtin_amdgcn_global_load_lds(gw, (__attribute__((address_space(3))) void*)(sbase + (wid * 8 + c) * 1024),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          gx, (__attribute__((address_space(3))) void*)(sbase + kTileI * kBK * 2 + (wid * 8 + c) * 1024), 16, 0, 0);
+  for (int c = 0; c < kChunks; ++c) {
+    const int64_t rw = min(w0 + c * 16 + (lane >> 2), w_last) - wb;
+    const int64_t rx = min(j0 + c * 16 + (lane >> 2), a.rows - 1) - jb;
+    w_off[c] = (uint32_t)(rw * K * 2 + piece * 16);
+    x_off[c] = (uint32_t)(rx * K * 2 + piece * 16);
+  }
+  auto lds_at = [&](int buf, bool tokens, int c) {
+    return smem + buf * kStageBytes + (tokens ? kTileI * kRowBytes : 0) + (wid * kChunks + c) * 1024;
+  };
+  // load i (0..7) of a full stage: weight chunk i / 2 (i even) or token chunk i / 2
+  auto load_full = [&](int64_t kb, int buf, int i) {
+    const int c = i >> 1;
+    if (i & 1)
+      __builtin_amdgcn_global_load_lds(wave_x + kb * 2 + x_off[c], (lds_void_ptr)lds_at(buf, true, c), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(wave_w + kb * 2 + w_off[c], (lds_void_ptr)lds_at(buf, false, c), 16, 0, 0);
+  };
+  // any stage, the last one possibly past K: pieces past K read a zero piece
+  auto load_stage = [&](int64_t kb, int buf) {
+    const bool full = kb + kBK <= K;
+    const bool in_k = full || kb + piece * 8 < K;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const void* gw = in_k ? (const void*)(wave_w + kb * 2 + w_off[c]) : (const void*)kZeroPiece;
+      const void* gx = in_k ? (const void*)(wave_x + kb * 2 + x_off[c]) : (const void*)kZeroPiece;
+      __builtin_amdgcn_global_load_lds(gw, (lds_void_ptr)lds_at(buf, false, c), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(gx, (lds_void_ptr)lds_at(buf, true, c), 16, 0, 0);
     }
   };
 
@@ -132,37 +168,117 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     for (int n = 0; n < 4; ++n) acc[m][n] = floatx16{};
 
   // fragment rows of this lane: weight rows wi*128 + m*32 + lane%32, token
-  // rows wj*128 + n*32 + lane%32 (both with (row / 2) & 7 == (lane % 32 / 2) & 7)
+  // rows wj*128 + n*32 + lane%32 (both with (row / 4) & 3 == (lane % 32 / 4) & 3)
   const int frow = lane & 31;
-  const int fswz = (frow >> 1) & 7;
+  const int fswz = (frow >> 2) & 3;
   const int nst = (int)((K + kBK - 1) / kBK);
-  load_stage(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) load_stage((int64_t)(st + 1) * kBK, buf ^ 1);
-    const uint8_t* wt = smem + buf * kStageBytes + (wi * 128 + frow) * 128;
-    const uint8_t* xt = smem + buf * kStageBytes + kTileI * kBK * 2 + (wj * 128 + frow) * 128;
+  auto read_frags = [&](int buf, int kk, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
+    const uint8_t* wt = smem + buf * kStageBytes + (wi * 128 + frow) * kRowBytes;
+    const uint8_t* xt = smem + buf * kStageBytes + kTileI * kRowBytes + (wj * 128 + frow) * kRowBytes;
+    const int off = ((kk * 2 + half) ^ fswz) * 16;
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int off = ((kk * 2 + half) ^ fswz) * 16;
-      bf16x8 af[4], bfr[4];
+    for (int m = 0; m < 4; ++m)
+      af[m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wt + m * 32 * kRowBytes + off));
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        af[m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wt + m * 32 * 128 + off));
+    for (int n = 0; n < 4; ++n)
+      bfr[n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xt + n * 32 * kRowBytes + off));
+  };
+  // the 16 MFMAs of one K-step: the first, then the other 15
+  auto first_mfma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
+    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bfr[0], acc[0][0], 0, 0, 0);
+  };
+  auto other_mfmas = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
-        bfr[n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xt + n * 32 * 128 + off));
+    for (int t = 1; t < 16; ++t)
+      acc[t >> 2][t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t >> 2], bfr[t & 3], acc[t >> 2][t & 3], 0, 0, 0);
+  };
+  // the same 15 with loads i0 .. i0 + 3 of a full stage issued after MFMAs 2,
+  // 5, 8 and 11: a stage's eight loads are spread over both K-steps, so that
+  // the four waves' loads come no faster than the texture path takes them
+  // (a load it cannot take yet stalls the wave, and the MFMAs behind it)
+  auto other_mfmas_loading = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], int64_t kb, int lbuf, int i0) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[m], bfr[n], acc[m][n], 0, 0, 0);
+    for (int t = 1; t < 16; ++t) {
+      acc[t >> 2][t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t >> 2], bfr[t & 3], acc[t >> 2][t & 3], 0, 0, 0);
+      if (t % 3 == 2 && t <= 11) load_full(kb, lbuf, i0 + t / 3);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads of the next stage have landed
-    __syncthreads();
-  }
+  };
+  // wait until a stage has landed, given the number of loads issued after its
+  // last one (loads complete in issue order), then make every wave's loads
+  // visible and every wave's earlier LDS reads complete
+  auto stage_landed = [&](int later) {
+    if (later >= 24)
+      wait_vmcnt<24>();
+    else if (later >= 20)
+      wait_vmcnt<20>();
+    else if (later >= 16)
+      wait_vmcnt<16>();
+    else if (later >= 12)
+      wait_vmcnt<12>();
+    else if (later >= 8)
+      wait_vmcnt<8>();
+    else if (later >= 4)
+      wait_vmcnt<4>();
+    else
+      wait_vmcnt<0>();
+    // lgkmcnt(0) + barrier, without the vmcnt(0) that a workgroup fence adds
+    // (it would also wait for the loads of the stages still ahead)
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("s_barrier" ::: "memory");
+  };
+
+  // Per stage st (its K-step 0 fragments already in registers): load stage
+  // ls = st + kStages - 1 into the buffer stage st - 1 used, read K-step 1
+  // while the MFMAs of K-step 0 run (after the first, so that the wait before
+  // it covers only the older reads), then (stage st + 1 landed) read its
+  // K-step 0 while the MFMAs of K-step 1 run.  A full stage's loads go half
+  // into each K-step's MFMAs; the last, partial one is loaded at once.  Every
+  // read of a stage's buffer is issued before the barrier of the iteration
+  // that computes it and has completed at that barrier (lgkmcnt(0)), so loads
+  // issued after it overwrite a buffer no wave still reads.
+  static_assert(kBK == 32 && kStages >= 3 && kStages <= 5 && kLoadsPerStage == 8,
+                "two K-steps per stage, eight loads per stage, at most three later stages in flight");
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  const int nst_full = (int)(K / kBK);   // stages entirely inside K
+  auto step = [&](int st, bool interleaved) __attribute__((always_inline)) {
+    const int buf = st % kStages;
+    const int ls = st + kStages - 1;
+    const int64_t lkb = (int64_t)ls * kBK;
+    if (!interleaved && ls < nst) load_stage(lkb, ls % kStages);
+    first_mfma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(buf, 1, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (interleaved)
+      other_mfmas_loading(a0, b0, lkb, ls % kStages, 0);
+    else
+      other_mfmas(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage st + 1; issued after it: the stages up to ls - 1 and half of ls
+    // (interleaved), else the stages up to min(ls, nst - 1).  In the last
+    // stage this waits for nothing and reads a buffer it never uses.
+    stage_landed(interleaved ? kLoadsPerStage * (kStages - 3) + kLoadsPerStage / 2
+                             : kLoadsPerStage * max(0, min(ls, nst - 1) - st - 1));
+    first_mfma(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags((st + 1) % kStages, 0, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (interleaved)
+      other_mfmas_loading(a1, b1, lkb, ls % kStages, kLoadsPerStage / 2);
+    else
+      other_mfmas(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int q = 0; q < kStages - 1; ++q)
+    if (q < nst) load_stage((int64_t)q * kBK, q);
+  stage_landed(kLoadsPerStage * min(kStages - 2, nst - 1));
+  read_frags(0, 0, a0, b0);
+  int st = 0;
+  // while the stage loaded is a full one, its loads go between MFMAs
+  for (; st + kStages - 1 < nst_full; ++st) step(st, true);
+  for (; st < nst; ++st) step(st, false);
 
   // epilogue: element e of tile (m, n) is weight row i0 + 8 (e / 4) + 4 half +
   // e % 4, token j = tj*256 + wj*128 + n*32 + lane % 32; four consecutive
