@@ -91,7 +91,11 @@ def check_rows(y_gpu, x_bits, wg_bits, wd_bits, where=""):
     return Y
 
 
-@pytest.mark.parametrize("rows,D,F", [(300, 256, 512), (1, 64, 8), (77, 128, 1000), (513, 512, 1536)])
+# K = D or F: whole 64-element stages, a partial last stage (1000, 200, 584,
+# 136, 72, 1096), a single partial stage (8); weight panels fewer than 8
+# (one XCD walk) and 9 (the shared walk, split unevenly over the XCDs)
+@pytest.mark.parametrize("rows,D,F", [(300, 256, 512), (1, 64, 8), (77, 128, 1000), (513, 512, 1536),
+                                      (130, 200, 584), (64, 136, 72), (300, 2304, 1096)])
 def test_ffn_small_shapes_all_rows(rows, D, F):
     rng_seed = rows + D + F
     wg = synth.uniform_bf16_bits(11 + rng_seed, 0, 2 * F, D, -4)

@@ -13,20 +13,25 @@
 //   2. down: i over the D rows of Wd, j over the tokens, K = F; y as bf16.
 // A workgroup computes a 256 (weight rows) x 256 (tokens) tile with
 // v_mfma_f32_32x32x16_bf16: four waves of 128 x 128, each holding 4 x 4
-// accumulator tiles.  Operands stream through a four-stage LDS ring with
-// gfx950's direct global-to-LDS 16-byte loads, 32 K-elements per stage, each
-// stage's loads issued three stages before it is consumed (the loads come from
-// L2 or further: one stage of lead left the waves waiting on them).  Rows are
-// 64 bytes; their 16-byte pieces are XOR-swizzled by (row / 4) & 3, so the 16
-// lanes of each pass of a fragment read hit 16 different bank groups.
+// accumulator tiles.  Operands stream through LDS with gfx950's direct
+// global-to-LDS 16-byte loads, 64 K-elements per stage in two stage buffers
+// (128 KB): a row's 128 bytes per stage make whole 128-byte L2 requests, which
+// halves the request count of 64-byte rows and is what the L1-to-L2 path,
+// bound by its outstanding requests, needs.  A stage's loads are spread
+// between the MFMAs (a burst stalls the waves at the texture unit), the next
+// K-step's fragments are read while the current one's MFMAs run, and the one
+// barrier per stage waits only for the stage it needs.  Pieces are
+// XOR-swizzled by (row / 2) & 7, so the 16 lanes of each pass of a fragment
+// read hit 16 different bank groups.  (The kernel also builds with 32
+// K-element stages, 64-byte rows, in a ring of three to five.)
 // In the gate/up launch the workgroup's 256 weight rows are 64 gate rows, the
 // 64 up rows of the same channels, then the next 64 of each: a wave's first
 // two accumulator rows of tiles are gate and its last two the matching up
 // channels, so gate and up of one (token, channel) sit in the same lane and
 // register.  Rows past the end are clamped (their results are not stored) and
-// K past the end reads a zero piece.  Workgroups are dealt to the XCDs so that
-// each XCD walks its own run of tiles, 8 token panels at a time, and the
-// workgroups running together share weight and token panels in their L2.
+// K past the end reads a zero piece.  The tile walk shares token panels
+// across the XCDs (through the MALL) and weight and token panels among the
+// workgroups of an XCD (through its L2).
 #include "../../include/uniprefill.h"
 #include "common.h"
 
@@ -40,11 +45,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kFfnThreads = 256;          // four waves
 constexpr int kTileI = 256;               // weight rows per workgroup
 constexpr int kTileJ = 256;               // tokens per workgroup
-constexpr int kBK = 32;                   // K elements per stage (64-byte rows)
-constexpr int kStages = 4;                // LDS ring depth; loads run kStages - 1 stages ahead
-constexpr int kRowBytes = kBK * 2;
-constexpr int kStageBytes = (kTileI + kTileJ) * kRowBytes;   // 32 KB
-constexpr int kLoadsPerStage = kStageBytes / 4 / 1024;       // 1 KB wave loads per wave per stage (8)
+constexpr int kBK = 64;                   // K elements per stage
+constexpr int kStages = 2;                // LDS ring depth
+constexpr int kRowBytes = kBK * 2;        // one row's bytes in a stage
+constexpr int kPieces = kRowBytes / 16;   // 16-byte pieces per row
+constexpr int kNK = kBK / 16;             // MFMA K-steps per stage
+constexpr int kStageBytes = (kTileI + kTileJ) * kRowBytes;
+constexpr int kRowsPerLoad = 1024 / kRowBytes;                // rows one 1 KB wave load covers
+constexpr int kChunks = 64 / kRowsPerLoad;                     // loads per operand per wave per stage
+constexpr int kLoadsPerStage = 2 * kChunks;                    // per wave
+// LDS pieces are XOR-swizzled by (row >> kSwzShift) & (kPieces - 1): the rows
+// that share a 256-byte window get distinct pieces
+constexpr int kSwzShift = kRowBytes == 64 ? 2 : 1;
+static_assert((kBK == 32 && kStages >= 3 && kStages <= 5) || (kBK == 64 && kStages == 2),
+              "the stage layouts and load schedules below");
+static_assert(kStages * kStageBytes <= 160 * 1024, "LDS");
 constexpr int kGroupJ = 8;                // token panels walked together
 
 __device__ __attribute__((aligned(16))) const uint32_t kZeroPiece[4] = {0u, 0u, 0u, 0u};
@@ -87,32 +102,51 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   const int wi = wid >> 1, wj = wid & 1;
   const int half = lane >> 5;
 
-  // tile of this workgroup: XCD x (= id mod 8) walks tiles [x T/8, (x+1) T/8)
-  // in order; a run of tiles covers kGroupJ token panels for each weight panel
-  const int64_t ntiles = (int64_t)a.tiles_i * a.tiles_j;
-  const int64_t per_xcd = (ntiles + 7) / 8;
-  const int64_t t = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (t >= ntiles) return;
-  const int64_t grp = t / ((int64_t)kGroupJ * a.tiles_i), wgi = t % ((int64_t)kGroupJ * a.tiles_i);
-  const int64_t gj = min((int64_t)kGroupJ, (int64_t)a.tiles_j - grp * kGroupJ);
-  const int ti = (int)(wgi / gj);
-  const int tj = (int)(grp * kGroupJ + wgi % gj);
+  // tile of this workgroup.  Workgroups are dealt to the 8 XCDs round-robin
+  // (XCD x = id mod 8 runs the ones with id / 8 = 0, 1, 2, ... in turn).
+  // With 8 or more weight panels, every XCD walks the same run of kGroupJ
+  // token panels at once, over its own eighth of the weight panels: a token
+  // panel leaves HBM once and the other XCDs' L2 misses on it hit the MALL.
+  // Otherwise XCD x walks tiles [x T/8, (x+1) T/8) in order.  Either way the
+  // workgroups of an XCD running together cover a few weight panels times
+  // kGroupJ token panels, which they share in its L2.
+  int ti, tj;
+  {
+    const int x = blockIdx.x & 7;
+    const int64_t q = blockIdx.x >> 3;
+    int64_t wgi, grp, gj, ti0;
+    if (a.tiles_i >= 8) {
+      ti0 = (int64_t)x * a.tiles_i / 8;
+      const int64_t nti = (int64_t)(x + 1) * a.tiles_i / 8 - ti0;
+      if (q >= nti * a.tiles_j) return;
+      grp = q / (nti * kGroupJ);
+      wgi = q % (nti * kGroupJ);
+    } else {
+      const int64_t ntiles = (int64_t)a.tiles_i * a.tiles_j;
+      const int64_t t = x * ((ntiles + 7) / 8) + q;
+      if (t >= ntiles) return;
+      ti0 = 0;
+      grp = t / ((int64_t)kGroupJ * a.tiles_i);
+      wgi = t % ((int64_t)kGroupJ * a.tiles_i);
+    }
+    gj = min((int64_t)kGroupJ, (int64_t)a.tiles_j - grp * kGroupJ);
+    ti = (int)(ti0 + wgi / gj);
+    tj = (int)(grp * kGroupJ + wgi % gj);
+  }
 
   const int64_t K = a.K;
   const int64_t n_w = kGateUp ? 2 * a.F : a.n_out;   // weight rows
 
-  // this wave's loads: chunk c (0..3) of its 64 weight rows and of its 64
-  // token rows covers 16 rows, tile row r = 16 (4 wid + c) + L / 4 for lane L,
-  // which fills LDS slot L % 4 of row r with global piece (L % 4) ^ ((r / 4) & 3)
-  // = (L % 4) ^ ((L / 16) & 3).  Rows past the end are clamped.  Each wave
+  // this wave's loads: chunk c of its 64 weight rows and of its 64 token rows
+  // covers kRowsPerLoad rows, tile row r = 64 wid + c kRowsPerLoad + L / kPieces
+  // for lane L, which fills LDS slot L % kPieces of row r with global piece
+  // (L % kPieces) ^ swizzle(r).  Rows past the end are clamped.  Each wave
   // addresses its rows from a uniform first-row pointer plus a fixed 32-bit
-  // lane offset (< 64 K 2 + 64 bytes), so a stage's loads need no vector
+  // lane offset (< 64 K 2 + 128 bytes), so a stage's loads need no vector
   // arithmetic.
   // In the gate/up launch tile rows [gate 64 | up 64 | gate 64 | up 64] are the
   // channels ti*128 + 0..127: wave wid holds gate (wid even) or up (wid odd)
   // rows of channels ti*128 + (wid / 2)*64 + 0..63.
-  constexpr int kChunks = kLoadsPerStage / 2;
-  const int piece = (lane & 3) ^ ((lane >> 4) & 3);
   int64_t w_first, w0, w_last;   // first weight row of the wave, unclamped first, last valid
   if (kGateUp) {
     const int64_t f0 = (int64_t)ti * 128 + (wid >> 1) * 64;
@@ -130,17 +164,22 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   const uint8_t* wave_w = reinterpret_cast<const uint8_t*>(a.w + (w_first + wb) * K);
   const uint8_t* wave_x = reinterpret_cast<const uint8_t*>(a.x + jb * K);
   uint32_t w_off[kChunks], x_off[kChunks];
+  int piece_of[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    const int64_t rw = min(w0 + c * 16 + (lane >> 2), w_last) - wb;
-    const int64_t rx = min(j0 + c * 16 + (lane >> 2), a.rows - 1) - jb;
-    w_off[c] = (uint32_t)(rw * K * 2 + piece * 16);
-    x_off[c] = (uint32_t)(rx * K * 2 + piece * 16);
+    const int rr = c * kRowsPerLoad + lane / kPieces;   // row within the wave's 64
+    const int r = wid * 64 + rr;
+    piece_of[c] = (lane % kPieces) ^ ((r >> kSwzShift) & (kPieces - 1));
+    const int64_t rw = min(w0 + rr, w_last) - wb;
+    const int64_t rx = min(j0 + rr, a.rows - 1) - jb;
+    w_off[c] = (uint32_t)(rw * K * 2 + piece_of[c] * 16);
+    x_off[c] = (uint32_t)(rx * K * 2 + piece_of[c] * 16);
   }
   auto lds_at = [&](int buf, bool tokens, int c) {
     return smem + buf * kStageBytes + (tokens ? kTileI * kRowBytes : 0) + (wid * kChunks + c) * 1024;
   };
-  // load i (0..7) of a full stage: weight chunk i / 2 (i even) or token chunk i / 2
+  // load i (0 .. kLoadsPerStage - 1) of a full stage: weight chunk i / 2 (i
+  // even) or token chunk i / 2
   auto load_full = [&](int64_t kb, int buf, int i) {
     const int c = i >> 1;
     if (i & 1)
@@ -148,16 +187,18 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     else
       __builtin_amdgcn_global_load_lds(wave_w + kb * 2 + w_off[c], (lds_void_ptr)lds_at(buf, false, c), 16, 0, 0);
   };
-  // any stage, the last one possibly past K: pieces past K read a zero piece
-  auto load_stage = [&](int64_t kb, int buf) {
+  // loads i0 .. i0 + n - 1 of any stage, the last one possibly past K: pieces
+  // past K read a zero piece
+  auto load_part = [&](int64_t kb, int buf, int i0, int n) {
     const bool full = kb + kBK <= K;
-    const bool in_k = full || kb + piece * 8 < K;
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const void* gw = in_k ? (const void*)(wave_w + kb * 2 + w_off[c]) : (const void*)kZeroPiece;
-      const void* gx = in_k ? (const void*)(wave_x + kb * 2 + x_off[c]) : (const void*)kZeroPiece;
-      __builtin_amdgcn_global_load_lds(gw, (lds_void_ptr)lds_at(buf, false, c), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(gx, (lds_void_ptr)lds_at(buf, true, c), 16, 0, 0);
+    for (int i = 0; i < kLoadsPerStage; ++i) {
+      if (i < i0 || i >= i0 + n) continue;
+      const int c = i >> 1;
+      const bool in_k = full || kb + piece_of[c] * 8 < K;
+      const uint8_t* base = (i & 1) ? wave_x + x_off[c] : wave_w + w_off[c];
+      const void* g = in_k ? (const void*)(base + kb * 2) : (const void*)kZeroPiece;
+      __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds_at(buf, i & 1, c), 16, 0, 0);
     }
   };
 
@@ -168,10 +209,12 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     for (int n = 0; n < 4; ++n) acc[m][n] = floatx16{};
 
   // fragment rows of this lane: weight rows wi*128 + m*32 + lane%32, token
-  // rows wj*128 + n*32 + lane%32 (both with (row / 4) & 3 == (lane % 32 / 4) & 3)
+  // rows wj*128 + n*32 + lane%32, whose swizzle is that of lane%32 (the tile
+  // offsets are multiples of the swizzle period)
   const int frow = lane & 31;
-  const int fswz = (frow >> 2) & 3;
+  const int fswz = (frow >> kSwzShift) & (kPieces - 1);
   const int nst = (int)((K + kBK - 1) / kBK);
+  const int nst_full = (int)(K / kBK);   // stages entirely inside K
   auto read_frags = [&](int buf, int kk, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
     const uint8_t* wt = smem + buf * kStageBytes + (wi * 128 + frow) * kRowBytes;
     const uint8_t* xt = smem + buf * kStageBytes + kTileI * kRowBytes + (wj * 128 + frow) * kRowBytes;
@@ -183,24 +226,19 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     for (int n = 0; n < 4; ++n)
       bfr[n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xt + n * 32 * kRowBytes + off));
   };
-  // the 16 MFMAs of one K-step: the first, then the other 15
+  // the 16 MFMAs of one K-step: the first, then the other 15, with loads
+  // i0 .. i0 + n - 1 of a full stage spread between them (a load the texture
+  // path cannot take yet stalls the wave, and the MFMAs behind it)
   auto first_mfma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
     acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bfr[0], acc[0][0], 0, 0, 0);
   };
-  auto other_mfmas = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
-#pragma unroll
-    for (int t = 1; t < 16; ++t)
-      acc[t >> 2][t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t >> 2], bfr[t & 3], acc[t >> 2][t & 3], 0, 0, 0);
-  };
-  // the same 15 with loads i0 .. i0 + 3 of a full stage issued after MFMAs 2,
-  // 5, 8 and 11: a stage's eight loads are spread over both K-steps, so that
-  // the four waves' loads come no faster than the texture path takes them
-  // (a load it cannot take yet stalls the wave, and the MFMAs behind it)
-  auto other_mfmas_loading = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], int64_t kb, int lbuf, int i0) {
+  auto other_mfmas = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], int64_t kb, int lbuf, int i0, int n) {
 #pragma unroll
     for (int t = 1; t < 16; ++t) {
       acc[t >> 2][t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t >> 2], bfr[t & 3], acc[t >> 2][t & 3], 0, 0, 0);
-      if (t % 3 == 2 && t <= 11) load_full(kb, lbuf, i0 + t / 3);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < n && t == 1 + q * 15 / n) load_full(kb, lbuf, i0 + q);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -228,57 +266,104 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     asm volatile("s_barrier" ::: "memory");
   };
 
-  // Per stage st (its K-step 0 fragments already in registers): load stage
-  // ls = st + kStages - 1 into the buffer stage st - 1 used, read K-step 1
-  // while the MFMAs of K-step 0 run (after the first, so that the wait before
-  // it covers only the older reads), then (stage st + 1 landed) read its
-  // K-step 0 while the MFMAs of K-step 1 run.  A full stage's loads go half
-  // into each K-step's MFMAs; the last, partial one is loaded at once.  Every
-  // read of a stage's buffer is issued before the barrier of the iteration
-  // that computes it and has completed at that barrier (lgkmcnt(0)), so loads
-  // issued after it overwrite a buffer no wave still reads.
-  static_assert(kBK == 32 && kStages >= 3 && kStages <= 5 && kLoadsPerStage == 8,
-                "two K-steps per stage, eight loads per stage, at most three later stages in flight");
+  // Iteration st computes stage st, K-step by K-step: the first MFMA, the
+  // reads of the next K-step's fragments, the other 15 MFMAs; before the last
+  // K-step's reads (those of stage st + 1's first K-step) the wave waits for
+  // stage st + 1 at a barrier.  Every read of a stage's buffer is issued
+  // before that barrier and has completed at it (lgkmcnt(0)), so loads issued
+  // after it may refill the buffer.
+  // Loads in the steady state (all stages involved full), spread over the
+  // K-steps' MFMAs:
+  //  - ring of three or more: iteration st loads stage st + kStages - 1 into
+  //    the buffer of stage st - 1, an equal share in each K-step; at the
+  //    barrier, the later stages' loads and the share already issued of this
+  //    one may still be in flight;
+  //  - ring of two: the buffer of stage st + 2 is stage st's, free after the
+  //    barrier of iteration st, so its first half is loaded in the last
+  //    K-step of iteration st and its second half in the first two of
+  //    iteration st + 1; at the barrier nothing issued later is in flight.
+  // Stages past the steady state (the last, partial one among them) are loaded
+  // whole at the top of the iteration before they are needed.
+  constexpr int kHalf = kLoadsPerStage / 2;
+  constexpr int kShare = kLoadsPerStage / kNK;
   bf16x8 a0[4], b0[4], a1[4], b1[4];
-  const int nst_full = (int)(K / kBK);   // stages entirely inside K
-  auto step = [&](int st, bool interleaved) __attribute__((always_inline)) {
-    const int buf = st % kStages;
-    const int ls = st + kStages - 1;
-    const int64_t lkb = (int64_t)ls * kBK;
-    if (!interleaved && ls < nst) load_stage(lkb, ls % kStages);
-    first_mfma(a0, b0);
+  auto kstep = [&](int st, int kk, bool steady) __attribute__((always_inline)) {
+    bf16x8(&ca)[4] = (kk & 1) ? a1 : a0;
+    bf16x8(&cb)[4] = (kk & 1) ? b1 : b0;
+    bf16x8(&na)[4] = (kk & 1) ? a0 : a1;
+    bf16x8(&nb)[4] = (kk & 1) ? b0 : b1;
+    int lst = 0, i0 = 0, n = 0;   // loads in this K-step: stage, first, count
+    if (steady) {
+      if (kStages >= 3) {
+        lst = st + kStages - 1; i0 = kk * kShare; n = kShare;
+      } else if (kk == kNK - 1) {
+        lst = st + 2; i0 = 0; n = kHalf;
+      } else if (kk < 2) {
+        lst = st + 1; i0 = kHalf + kk * (kHalf / 2); n = kHalf / 2;
+      }
+    }
+    if (kk < kNK - 1) {
+      first_mfma(ca, cb);
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(st % kStages, kk + 1, na, nb);
+    } else {
+      int later;
+      if (steady)
+        later = kStages >= 3 ? kLoadsPerStage * (kStages - 3) + kShare * (kNK - 1) : 0;
+      else
+        later = kStages >= 3 ? kLoadsPerStage * max(0, min(st + kStages - 1, nst - 1) - st - 1) : 0;
+      // in the last stage this waits for nothing and reads a buffer it never uses
+      stage_landed(later);
+      first_mfma(ca, cb);
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags((st + 1) % kStages, 0, na, nb);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(buf, 1, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (interleaved)
-      other_mfmas_loading(a0, b0, lkb, ls % kStages, 0);
-    else
-      other_mfmas(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    // stage st + 1; issued after it: the stages up to ls - 1 and half of ls
-    // (interleaved), else the stages up to min(ls, nst - 1).  In the last
-    // stage this waits for nothing and reads a buffer it never uses.
-    stage_landed(interleaved ? kLoadsPerStage * (kStages - 3) + kLoadsPerStage / 2
-                             : kLoadsPerStage * max(0, min(ls, nst - 1) - st - 1));
-    first_mfma(a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags((st + 1) % kStages, 0, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (interleaved)
-      other_mfmas_loading(a1, b1, lkb, ls % kStages, kLoadsPerStage / 2);
-    else
-      other_mfmas(a1, b1);
+    other_mfmas(ca, cb, (int64_t)lst * kBK, lst % kStages, i0, n);
     __builtin_amdgcn_sched_barrier(0);
   };
+  auto iteration = [&](int st, bool steady) __attribute__((always_inline)) {
+    if (!steady) {
+      // a ring of three or more loads stage st + kStages - 1 here; a ring of
+      // two, stage st + 1 (its first half, when the steady state loaded it)
+      if (kStages >= 3) {
+        const int ls = st + kStages - 1;
+        if (ls < nst) load_part((int64_t)ls * kBK, ls % kStages, 0, kLoadsPerStage);
+      } else if (st + 1 < nst) {
+        // a full stage had its first half loaded (by the prologue or by
+        // steady iteration st - 1), a partial one nothing
+        const bool half_done = st + 1 < nst_full;
+        load_part((int64_t)(st + 1) * kBK, (st + 1) % kStages, half_done ? kHalf : 0,
+                  half_done ? kHalf : kLoadsPerStage);
+      }
+    }
 #pragma unroll
-  for (int q = 0; q < kStages - 1; ++q)
-    if (q < nst) load_stage((int64_t)q * kBK, q);
-  stage_landed(kLoadsPerStage * min(kStages - 2, nst - 1));
+    for (int kk = 0; kk < kNK; ++kk) kstep(st, kk, steady);
+  };
+
+  // prologue: a ring of three or more loads stages 0 .. kStages - 2, a ring of
+  // two stage 0 and the first half of stage 1 (when full), as the iterations
+  // before would have
+  int pro_later;
+  if (kStages >= 3) {
+#pragma unroll
+    for (int q = 0; q < kStages - 1; ++q)
+      if (q < nst) load_part((int64_t)q * kBK, q, 0, kLoadsPerStage);
+    pro_later = kLoadsPerStage * min(kStages - 2, nst - 1);
+  } else {
+    load_part(0, 0, 0, kLoadsPerStage);
+    pro_later = 0;
+    if (1 < nst_full) {
+      load_part(kBK, 1, 0, kHalf);
+      pro_later = kHalf;
+    }
+  }
+  stage_landed(pro_later);
   read_frags(0, 0, a0, b0);
+  const int steady_end = max(0, nst_full - (kStages >= 3 ? kStages - 1 : 2));
   int st = 0;
-  // while the stage loaded is a full one, its loads go between MFMAs
-  for (; st + kStages - 1 < nst_full; ++st) step(st, true);
-  for (; st < nst; ++st) step(st, false);
+  for (; st < steady_end; ++st) iteration(st, true);
+  for (; st < nst; ++st) iteration(st, false);
 
   // epilogue: element e of tile (m, n) is weight row i0 + 8 (e / 4) + 4 half +
   // e % 4, token j = tj*256 + wj*128 + n*32 + lane % 32; four consecutive
@@ -328,9 +413,13 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   }
 }
 
+// workgroups the kernel's tile walk takes
+int64_t ffn_gemm_grid(int64_t tiles_i, int64_t tiles_j) {
+  return tiles_i >= 8 ? 8 * ((tiles_i + 7) / 8) * tiles_j : (tiles_i * tiles_j + 7) / 8 * 8;
+}
+
 static hipError_t launch_ffn_gemm(bool gate_up, const FfnGemmArgs& a, hipStream_t s) {
-  const int64_t ntiles = (int64_t)a.tiles_i * a.tiles_j;
-  const unsigned grid = (unsigned)((ntiles + 7) / 8 * 8);
+  const unsigned grid = (unsigned)ffn_gemm_grid(a.tiles_i, a.tiles_j);
   if (gate_up)
     hipLaunchKernelGGL(ffn_gemm_kernel<true>, dim3(grid), dim3(kFfnThreads), 0, s, a);
   else
@@ -371,8 +460,9 @@ up_status up_ffn_forward(int32_t hidden, int32_t intermediate, const void* x, in
   const int64_t D = hidden, F = intermediate;
   const int64_t tj = (rows + up::kTileJ - 1) / up::kTileJ;
   const int64_t ti1 = (F + 127) / 128, ti2 = (D + up::kTileI - 1) / up::kTileI;
-  // token-panel and tile counts must fit the 32-bit grid
-  if (tj > INT32_MAX || ti1 * tj > (int64_t)UINT32_MAX - 8 || ti2 * tj > (int64_t)UINT32_MAX - 8)
+  // panel counts and the grids must fit 32 bits
+  if (tj > INT32_MAX || ti1 > INT32_MAX || up::ffn_gemm_grid(ti1, tj) > (int64_t)UINT32_MAX ||
+      up::ffn_gemm_grid(ti2, tj) > (int64_t)UINT32_MAX)
     return UP_ERR_SHAPE;
   if (workspace_bytes < up_ffn_workspace_bytes(hidden, intermediate, rows)) return UP_ERR_WORKSPACE;
   uint16_t* h = static_cast<uint16_t*>(workspace);
