@@ -14,16 +14,17 @@
 // A workgroup computes a 256 (weight rows) x 256 (tokens) tile with
 // v_mfma_f32_32x32x16_bf16: four waves of 128 x 128, each holding 4 x 4
 // accumulator tiles.  Operands stream through LDS with gfx950's direct
-// global-to-LDS 16-byte loads, 64 K-elements per stage in two stage buffers
-// (128 KB): a row's 128 bytes per stage make whole 128-byte L2 requests, which
-// halves the request count of 64-byte rows and is what the L1-to-L2 path,
-// bound by its outstanding requests, needs.  A stage's loads are spread
-// between the MFMAs (a burst stalls the waves at the texture unit), the next
-// K-step's fragments are read while the current one's MFMAs run, and the one
-// barrier per stage waits only for the stage it needs.  Pieces are
-// XOR-swizzled by (row / 2) & 7, so the 16 lanes of each pass of a fragment
-// read hit 16 different bank groups.  (The kernel also builds with 32
-// K-element stages, 64-byte rows, in a ring of three to five.)
+// global-to-LDS 16-byte loads in stages of 64 K-elements: a row's 128 bytes
+// per stage make whole 128-byte L2 requests (64-byte rows took twice the
+// requests, and the L1-to-L2 path is what bounds the kernel).  The 160 KB of
+// LDS hold a ring of five operand units (one operand's 256 rows of a stage,
+// 32 KB each), so the loads of a unit are issued one to two stages before it
+// is read, spread between the MFMAs (a burst stalls the waves at the texture
+// unit); they are buffer loads whose only per-stage change is a scalar
+// offset.  The next K-step's fragments are read while the current one's MFMAs
+// run, and the one barrier per stage waits only for the stage it needs.
+// Pieces are XOR-swizzled by (row / 2) & 7, so the 16 lanes of each pass of a
+// fragment read hit 16 different bank groups.
 // In the gate/up launch the workgroup's 256 weight rows are 64 gate rows, the
 // 64 up rows of the same channels, then the next 64 of each: a wave's first
 // two accumulator rows of tiles are gate and its last two the matching up
@@ -46,20 +47,17 @@ constexpr int kFfnThreads = 256;          // four waves
 constexpr int kTileI = 256;               // weight rows per workgroup
 constexpr int kTileJ = 256;               // tokens per workgroup
 constexpr int kBK = 64;                   // K elements per stage
-constexpr int kStages = 2;                // LDS ring depth
-constexpr int kRowBytes = kBK * 2;        // one row's bytes in a stage
-constexpr int kPieces = kRowBytes / 16;   // 16-byte pieces per row
-constexpr int kNK = kBK / 16;             // MFMA K-steps per stage
-constexpr int kStageBytes = (kTileI + kTileJ) * kRowBytes;
-constexpr int kRowsPerLoad = 1024 / kRowBytes;                // rows one 1 KB wave load covers
-constexpr int kChunks = 64 / kRowsPerLoad;                     // loads per operand per wave per stage
-constexpr int kLoadsPerStage = 2 * kChunks;                    // per wave
-// LDS pieces are XOR-swizzled by (row >> kSwzShift) & (kPieces - 1): the rows
-// that share a 256-byte window get distinct pieces
-constexpr int kSwzShift = kRowBytes == 64 ? 2 : 1;
-static_assert((kBK == 32 && kStages >= 3 && kStages <= 5) || (kBK == 64 && kStages == 2),
-              "the stage layouts and load schedules below");
-static_assert(kStages * kStageBytes <= 160 * 1024, "LDS");
+constexpr int kRowBytes = kBK * 2;        // one row's bytes in a stage (128)
+constexpr int kPieces = kRowBytes / 16;   // 16-byte pieces per row (8)
+constexpr int kNK = kBK / 16;             // MFMA K-steps per stage (4)
+constexpr int kUnitBytes = 256 * kRowBytes;   // one operand's 256 rows of a stage (32 KB)
+constexpr int kUnits = 5;                 // LDS ring of operand units (160 KB)
+constexpr int kRowsPerLoad = 1024 / kRowBytes;   // rows one 1 KB wave load covers (8)
+constexpr int kChunks = 64 / kRowsPerLoad;       // loads per operand per wave per stage (8)
+// LDS pieces are XOR-swizzled by (row / 2) & 7: the 16 rows that share a
+// 256-byte window of banks get distinct pieces
+constexpr int kSwzShift = 1;
+static_assert(kTileI == 256 && kTileJ == 256 && kUnits * kUnitBytes <= 160 * 1024, "LDS");
 constexpr int kGroupJ = 8;                // token panels walked together
 
 __device__ __attribute__((aligned(16))) const uint32_t kZeroPiece[4] = {0u, 0u, 0u, 0u};
@@ -89,6 +87,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// buffer descriptor word 3 for raw 32-bit-element loads on gfx9-family parts
+// (data format 32, no swizzle, no thread-id addressing)
+constexpr int kRawBufferFlags = 0x00020000;
+
 // a pointer in the LDS address space, as the direct-to-LDS loads take it (cast
 // at the call: a helper, or a lambda, that returns one loses the kernel's
 // host-side launch stub)
@@ -96,7 +98,7 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 template <bool kGateUp>
 __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kUnits * kUnitBytes];
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wi = wid >> 1, wj = wid & 1;
@@ -175,30 +177,37 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     w_off[c] = (uint32_t)(rw * K * 2 + piece_of[c] * 16);
     x_off[c] = (uint32_t)(rx * K * 2 + piece_of[c] * 16);
   }
-  auto lds_at = [&](int buf, bool tokens, int c) {
-    return smem + buf * kStageBytes + (tokens ? kTileI * kRowBytes : 0) + (wid * kChunks + c) * 1024;
-  };
-  // load i (0 .. kLoadsPerStage - 1) of a full stage: weight chunk i / 2 (i
-  // even) or token chunk i / 2
-  auto load_full = [&](int64_t kb, int buf, int i) {
-    const int c = i >> 1;
-    if (i & 1)
-      __builtin_amdgcn_global_load_lds(wave_x + kb * 2 + x_off[c], (lds_void_ptr)lds_at(buf, true, c), 16, 0, 0);
+  // Operand units: unit u is operand u % 2 (0 weights, 1 tokens) of stage
+  // u / 2, 256 rows of 128 bytes in LDS buffer u % kUnits.
+  auto unit_lds = [&](int u) { return smem + (u % kUnits) * kUnitBytes; };
+  // load c (0 .. 7) of unit u, a full stage: a buffer load from the wave's
+  // first row (raw, unswizzled descriptor) with the lane offset in the VGPR and
+  // the stage's K position in the scalar offset, so it takes no vector
+  // arithmetic at all; lane offset plus K position stay below 128 K 2 <= 2^31,
+  // the descriptor's range
+  const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc((void*)wave_w, (short)0, 0x7FFFFFFF, kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc((void*)wave_x, (short)0, 0x7FFFFFFF, kRawBufferFlags);
+  auto load_full = [&](int u, int c) {
+    const int kb2 = (u >> 1) * (2 * kBK);
+    uint8_t* dst = unit_lds(u) + (wid * kChunks + c) * 1024;
+    if (u & 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_x, (lds_void_ptr)dst, 16, x_off[c], kb2, 0, 0);
     else
-      __builtin_amdgcn_global_load_lds(wave_w + kb * 2 + w_off[c], (lds_void_ptr)lds_at(buf, false, c), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (lds_void_ptr)dst, 16, w_off[c], kb2, 0, 0);
   };
-  // loads i0 .. i0 + n - 1 of any stage, the last one possibly past K: pieces
-  // past K read a zero piece
-  auto load_part = [&](int64_t kb, int buf, int i0, int n) {
+  // loads c0 .. 7 of unit u of any stage, the last one possibly past K:
+  // pieces past K read a zero piece
+  auto load_unit = [&](int u, int c0) {
+    const int64_t kb = (int64_t)(u >> 1) * kBK;
     const bool full = kb + kBK <= K;
+    const uint8_t* base = (u & 1) ? wave_x : wave_w;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerStage; ++i) {
-      if (i < i0 || i >= i0 + n) continue;
-      const int c = i >> 1;
+    for (int c = 0; c < kChunks; ++c) {
+      if (c < c0) continue;
       const bool in_k = full || kb + piece_of[c] * 8 < K;
-      const uint8_t* base = (i & 1) ? wave_x + x_off[c] : wave_w + w_off[c];
-      const void* g = in_k ? (const void*)(base + kb * 2) : (const void*)kZeroPiece;
-      __builtin_amdgcn_global_load_lds(g, (lds_void_ptr)lds_at(buf, i & 1, c), 16, 0, 0);
+      const uint8_t* g = base + ((u & 1) ? x_off[c] : w_off[c]) + kb * 2;
+      __builtin_amdgcn_global_load_lds(in_k ? (const void*)g : (const void*)kZeroPiece,
+                                       (lds_void_ptr)(unit_lds(u) + (wid * kChunks + c) * 1024), 16, 0, 0);
     }
   };
 
@@ -215,9 +224,9 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   const int fswz = (frow >> kSwzShift) & (kPieces - 1);
   const int nst = (int)((K + kBK - 1) / kBK);
   const int nst_full = (int)(K / kBK);   // stages entirely inside K
-  auto read_frags = [&](int buf, int kk, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
-    const uint8_t* wt = smem + buf * kStageBytes + (wi * 128 + frow) * kRowBytes;
-    const uint8_t* xt = smem + buf * kStageBytes + kTileI * kRowBytes + (wj * 128 + frow) * kRowBytes;
+  auto read_frags = [&](int st, int kk, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
+    const uint8_t* wt = unit_lds(2 * st) + (wi * 128 + frow) * kRowBytes;
+    const uint8_t* xt = unit_lds(2 * st + 1) + (wj * 128 + frow) * kRowBytes;
     const int off = ((kk * 2 + half) ^ fswz) * 16;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -226,19 +235,28 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     for (int n = 0; n < 4; ++n)
       bfr[n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xt + n * 32 * kRowBytes + off));
   };
-  // the 16 MFMAs of one K-step: the first, then the other 15, with loads
-  // i0 .. i0 + n - 1 of a full stage spread between them (a load the texture
-  // path cannot take yet stalls the wave, and the MFMAs behind it)
+
+  // Load sequence j: the 16 loads of units 2j + 5 (tokens of stage j + 2) and
+  // 2j + 6 (weights of stage j + 3), in that order.  Their buffers are those
+  // of stage j's two units, free once every wave is past the barrier of
+  // iteration j.
+  constexpr int kN3 = 8, kN0 = 4, kN1 = 4;       // loads per K-step (K-step 3, then 0, 1, 2)
+  constexpr int kN2 = 2 * kChunks - kN3 - kN0 - kN1;
+  static_assert(kN3 <= kChunks && kN0 <= 8 && kN1 <= 8 && kN2 >= 0 && kN2 <= 8, "load spread");
+  auto load_seq = [&](int j, int p) { load_full(2 * j + 5 + (p >> 3), p & 7); };
+  // the 16 MFMAs of one K-step: the first, then the other 15 with positions
+  // p0 .. p0 + n - 1 of load sequence j spread between them (a load the
+  // texture path cannot take yet stalls the wave, and the MFMAs behind it)
   auto first_mfma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
     acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bfr[0], acc[0][0], 0, 0, 0);
   };
-  auto other_mfmas = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], int64_t kb, int lbuf, int i0, int n) {
+  auto other_mfmas = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], int j, int p0, int n) {
 #pragma unroll
     for (int t = 1; t < 16; ++t) {
       acc[t >> 2][t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t >> 2], bfr[t & 3], acc[t >> 2][t & 3], 0, 0, 0);
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        if (q < n && t == 1 + q * 15 / n) load_full(kb, lbuf, i0 + q);
+        if (q < n && t == 1 + q * 15 / n) load_seq(j, p0 + q);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -246,22 +264,14 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   // last one (loads complete in issue order), then make every wave's loads
   // visible and every wave's earlier LDS reads complete
   auto stage_landed = [&](int later) {
-    if (later >= 24)
-      wait_vmcnt<24>();
-    else if (later >= 20)
-      wait_vmcnt<20>();
-    else if (later >= 16)
+    if (later >= 16)
       wait_vmcnt<16>();
-    else if (later >= 12)
-      wait_vmcnt<12>();
     else if (later >= 8)
       wait_vmcnt<8>();
-    else if (later >= 4)
-      wait_vmcnt<4>();
     else
       wait_vmcnt<0>();
     // lgkmcnt(0) + barrier, without the vmcnt(0) that a workgroup fence adds
-    // (it would also wait for the loads of the stages still ahead)
+    // (it would also wait for the loads still ahead)
     __builtin_amdgcn_s_waitcnt(0xC07F);
     asm volatile("s_barrier" ::: "memory");
   };
@@ -269,100 +279,80 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   // Iteration st computes stage st, K-step by K-step: the first MFMA, the
   // reads of the next K-step's fragments, the other 15 MFMAs; before the last
   // K-step's reads (those of stage st + 1's first K-step) the wave waits for
-  // stage st + 1 at a barrier.  Every read of a stage's buffer is issued
-  // before that barrier and has completed at it (lgkmcnt(0)), so loads issued
-  // after it may refill the buffer.
-  // Loads in the steady state (all stages involved full), spread over the
-  // K-steps' MFMAs:
-  //  - ring of three or more: iteration st loads stage st + kStages - 1 into
-  //    the buffer of stage st - 1, an equal share in each K-step; at the
-  //    barrier, the later stages' loads and the share already issued of this
-  //    one may still be in flight;
-  //  - ring of two: the buffer of stage st + 2 is stage st's, free after the
-  //    barrier of iteration st, so its first half is loaded in the last
-  //    K-step of iteration st and its second half in the first two of
-  //    iteration st + 1; at the barrier nothing issued later is in flight.
-  // Stages past the steady state (the last, partial one among them) are loaded
-  // whole at the top of the iteration before they are needed.
-  constexpr int kHalf = kLoadsPerStage / 2;
-  constexpr int kShare = kLoadsPerStage / kNK;
+  // stage st + 1 at a barrier.  Every read of a stage's units is issued before
+  // that barrier and has completed at it (lgkmcnt(0)).
+  // Steady state (all units involved full): iteration st issues positions
+  // kN3 .. 15 of sequence st - 1 in K-steps 0 .. 2 and positions 0 .. kN3 - 1
+  // of sequence st after its barrier, in K-step 3.  At the barrier, stage
+  // st + 1's tokens are positions 0 .. 7 of sequence st - 1, and the 8 loads
+  // issued after them may still be in flight.
+  // Past the steady state, units are issued whole at the top of the iteration
+  // (the last stage possibly partial), up to unit 2 st + 4, whose buffer was
+  // freed at the barrier before.
+  int next_unit = 0, partial = 0;   // first unit not fully issued; loads of it issued
+  auto top_up = [&](int st) -> int {   // returns the loads issued after unit 2 st + 3
+    int later = 0;
+    while (next_unit <= 2 * st + 4 && (next_unit >> 1) < nst) {
+      load_unit(next_unit, partial);
+      if (next_unit > 2 * st + 3) later += kChunks - partial;
+      ++next_unit;
+      partial = 0;
+    }
+    return later;
+  };
   bf16x8 a0[4], b0[4], a1[4], b1[4];
-  auto kstep = [&](int st, int kk, bool steady) __attribute__((always_inline)) {
+  auto kstep = [&](int st, int kk, bool steady, int later) __attribute__((always_inline)) {
     bf16x8(&ca)[4] = (kk & 1) ? a1 : a0;
     bf16x8(&cb)[4] = (kk & 1) ? b1 : b0;
     bf16x8(&na)[4] = (kk & 1) ? a0 : a1;
     bf16x8(&nb)[4] = (kk & 1) ? b0 : b1;
-    int lst = 0, i0 = 0, n = 0;   // loads in this K-step: stage, first, count
+    int j = 0, p0 = 0, n = 0;
     if (steady) {
-      if (kStages >= 3) {
-        lst = st + kStages - 1; i0 = kk * kShare; n = kShare;
-      } else if (kk == kNK - 1) {
-        lst = st + 2; i0 = 0; n = kHalf;
-      } else if (kk < 2) {
-        lst = st + 1; i0 = kHalf + kk * (kHalf / 2); n = kHalf / 2;
-      }
+      if (kk == kNK - 1) { j = st; p0 = 0; n = kN3; }
+      else if (kk == 0) { j = st - 1; p0 = kN3; n = kN0; }
+      else if (kk == 1) { j = st - 1; p0 = kN3 + kN0; n = kN1; }
+      else { j = st - 1; p0 = kN3 + kN0 + kN1; n = kN2; }
     }
     if (kk < kNK - 1) {
       first_mfma(ca, cb);
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(st % kStages, kk + 1, na, nb);
+      read_frags(st, kk + 1, na, nb);
     } else {
-      int later;
-      if (steady)
-        later = kStages >= 3 ? kLoadsPerStage * (kStages - 3) + kShare * (kNK - 1) : 0;
-      else
-        later = kStages >= 3 ? kLoadsPerStage * max(0, min(st + kStages - 1, nst - 1) - st - 1) : 0;
-      // in the last stage this waits for nothing and reads a buffer it never uses
+      // in the last stage this waits for everything and reads units it never uses
       stage_landed(later);
       first_mfma(ca, cb);
       __builtin_amdgcn_sched_barrier(0);
-      read_frags((st + 1) % kStages, 0, na, nb);
+      read_frags(st + 1, 0, na, nb);
     }
     __builtin_amdgcn_sched_barrier(0);
-    other_mfmas(ca, cb, (int64_t)lst * kBK, lst % kStages, i0, n);
+    other_mfmas(ca, cb, j, p0, n);
     __builtin_amdgcn_sched_barrier(0);
   };
   auto iteration = [&](int st, bool steady) __attribute__((always_inline)) {
-    if (!steady) {
-      // a ring of three or more loads stage st + kStages - 1 here; a ring of
-      // two, stage st + 1 (its first half, when the steady state loaded it)
-      if (kStages >= 3) {
-        const int ls = st + kStages - 1;
-        if (ls < nst) load_part((int64_t)ls * kBK, ls % kStages, 0, kLoadsPerStage);
-      } else if (st + 1 < nst) {
-        // a full stage had its first half loaded (by the prologue or by
-        // steady iteration st - 1), a partial one nothing
-        const bool half_done = st + 1 < nst_full;
-        load_part((int64_t)(st + 1) * kBK, (st + 1) % kStages, half_done ? kHalf : 0,
-                  half_done ? kHalf : kLoadsPerStage);
-      }
-    }
+    const int later = steady ? kChunks : top_up(st);
 #pragma unroll
-    for (int kk = 0; kk < kNK; ++kk) kstep(st, kk, steady);
+    for (int kk = 0; kk < kNK; ++kk) kstep(st, kk, steady, later);
   };
 
-  // prologue: a ring of three or more loads stages 0 .. kStages - 2, a ring of
-  // two stage 0 and the first half of stage 1 (when full), as the iterations
-  // before would have
-  int pro_later;
-  if (kStages >= 3) {
+  // iterations 0 .. steady_end - 1 are steady: sequences -1 .. steady_end - 1
+  // are of full units
+  const int steady_end = max(0, nst_full - 3);
+  // prologue: stage 0 and the weights of stage 1, then (when iteration 0 is
+  // steady) the first positions of sequence -1, as iteration -1 would have
+  int pro_later = top_up(-1);
+  if (steady_end > 0) {
 #pragma unroll
-    for (int q = 0; q < kStages - 1; ++q)
-      if (q < nst) load_part((int64_t)q * kBK, q, 0, kLoadsPerStage);
-    pro_later = kLoadsPerStage * min(kStages - 2, nst - 1);
-  } else {
-    load_part(0, 0, 0, kLoadsPerStage);
-    pro_later = 0;
-    if (1 < nst_full) {
-      load_part(kBK, 1, 0, kHalf);
-      pro_later = kHalf;
-    }
+    for (int p = 0; p < kN3; ++p) load_seq(-1, p);
+    pro_later += kN3;
   }
   stage_landed(pro_later);
   read_frags(0, 0, a0, b0);
-  const int steady_end = max(0, nst_full - (kStages >= 3 ? kStages - 1 : 2));
   int st = 0;
   for (; st < steady_end; ++st) iteration(st, true);
+  if (steady_end > 0) {   // sequence steady_end - 1 was begun
+    next_unit = 2 * steady_end + 3;
+    partial = kN3;
+  }
   for (; st < nst; ++st) iteration(st, false);
 
   // epilogue: element e of tile (m, n) is weight row i0 + 8 (e / 4) + 4 half +
