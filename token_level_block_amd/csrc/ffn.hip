@@ -12,7 +12,9 @@
 //      the registers);
 //   2. down: i over the D rows of Wd, j over the tokens, K = F; y as bf16.
 // A workgroup computes a 256 (weight rows) x 256 (tokens) tile with
-// v_mfma_f32_32x32x16_bf16: four waves of 128 x 128, each holding 4 x 4
+// v_mfma_f32_32x32x16_bf16: eight waves (two per SIMD, so that one wave's
+// stall on a load it cannot issue yet leaves the other issuing MFMAs) of
+// 128 x 64, each holding 4 x 2
 // accumulator tiles.  Operands stream through LDS with gfx950's direct
 // global-to-LDS 16-byte loads in stages of 64 K-elements: a row's 128 bytes
 // per stage make whole 128-byte L2 requests (64-byte rows took twice the
@@ -43,7 +45,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kFfnThreads = 256;          // four waves
+constexpr int kWaves = 8;                 // two per SIMD
+constexpr int kFfnThreads = 64 * kWaves;
 constexpr int kTileI = 256;               // weight rows per workgroup
 constexpr int kTileJ = 256;               // tokens per workgroup
 constexpr int kBK = 64;                   // K elements per stage
@@ -53,7 +56,13 @@ constexpr int kNK = kBK / 16;             // MFMA K-steps per stage (4)
 constexpr int kUnitBytes = 256 * kRowBytes;   // one operand's 256 rows of a stage (32 KB)
 constexpr int kUnits = 5;                 // LDS ring of operand units (160 KB)
 constexpr int kRowsPerLoad = 1024 / kRowBytes;   // rows one 1 KB wave load covers (8)
-constexpr int kChunks = 64 / kRowsPerLoad;       // loads per operand per wave per stage (8)
+constexpr int kWaveRows = 256 / kWaves;         // rows of each unit one wave loads
+constexpr int kChunks = kWaveRows / kRowsPerLoad;  // loads per operand per wave per stage
+// wave tile: 128 weight rows (4 MFMA tiles) x kWaveTok tokens (kNT tiles)
+constexpr int kWaveTok = kTileJ / (kWaves / 2);
+constexpr int kNT = kWaveTok / 32;
+constexpr int kTiles = 4 * kNT;                    // MFMAs per K-step per wave
+static_assert(kWaves == 4 || kWaves == 8, "wave layouts");
 // LDS pieces are XOR-swizzled by (row / 2) & 7: the 16 rows that share a
 // 256-byte window of banks get distinct pieces
 constexpr int kSwzShift = 1;
@@ -101,7 +110,7 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   __shared__ __attribute__((aligned(16))) uint8_t smem[kUnits * kUnitBytes];
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wi = wid >> 1, wj = wid & 1;
+  const int wi = wid / (kWaves / 2), wj = wid % (kWaves / 2);
   const int half = lane >> 5;
 
   // tile of this workgroup.  Workgroups are dealt to the 8 XCDs round-robin
@@ -139,29 +148,30 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   const int64_t K = a.K;
   const int64_t n_w = kGateUp ? 2 * a.F : a.n_out;   // weight rows
 
-  // this wave's loads: chunk c of its 64 weight rows and of its 64 token rows
-  // covers kRowsPerLoad rows, tile row r = 64 wid + c kRowsPerLoad + L / kPieces
-  // for lane L, which fills LDS slot L % kPieces of row r with global piece
-  // (L % kPieces) ^ swizzle(r).  Rows past the end are clamped.  Each wave
-  // addresses its rows from a uniform first-row pointer plus a fixed 32-bit
-  // lane offset (< 64 K 2 + 128 bytes), so a stage's loads need no vector
-  // arithmetic.
+  // this wave's loads: chunk c of its kWaveRows weight rows and of its
+  // kWaveRows token rows covers kRowsPerLoad rows, tile row r = kWaveRows wid
+  // + c kRowsPerLoad + L / kPieces for lane L, which fills LDS slot L % kPieces
+  // of row r with global piece (L % kPieces) ^ swizzle(r).  Rows past the end
+  // are clamped.  Each wave addresses its rows from a uniform first-row
+  // pointer plus a fixed 32-bit lane offset (< 64 K 2 + 128 bytes), so a
+  // stage's loads need no vector arithmetic.
   // In the gate/up launch tile rows [gate 64 | up 64 | gate 64 | up 64] are the
-  // channels ti*128 + 0..127: wave wid holds gate (wid even) or up (wid odd)
-  // rows of channels ti*128 + (wid / 2)*64 + 0..63.
+  // channels ti*128 + 0..127: the wave's rows rb .. rb + kWaveRows - 1 (rb =
+  // kWaveRows wid) are up rows when (rb / 64) is odd, of channels ti*128 +
+  // (rb / 128)*64 + rb % 64 + 0, 1, ...
+  const int rb = wid * kWaveRows;
   int64_t w_first, w0, w_last;   // first weight row of the wave, unclamped first, last valid
   if (kGateUp) {
-    const int64_t f0 = (int64_t)ti * 128 + (wid >> 1) * 64;
-    w0 = f0;
+    w0 = (int64_t)ti * 128 + (rb >> 7) * 64 + (rb & 63);
     w_last = a.F - 1;
-    w_first = (wid & 1) ? a.F : 0;   // gate or up half
+    w_first = ((rb >> 6) & 1) ? a.F : 0;   // gate or up half
   } else {
-    w0 = (int64_t)ti * kTileI + wid * 64;
+    w0 = (int64_t)ti * kTileI + rb;
     w_last = n_w - 1;
     w_first = 0;
   }
   const int64_t wb = min(w0, w_last);
-  const int64_t j0 = (int64_t)tj * kTileJ + wid * 64;
+  const int64_t j0 = (int64_t)tj * kTileJ + rb;
   const int64_t jb = min(j0, a.rows - 1);
   const uint8_t* wave_w = reinterpret_cast<const uint8_t*>(a.w + (w_first + wb) * K);
   const uint8_t* wave_x = reinterpret_cast<const uint8_t*>(a.x + jb * K);
@@ -169,8 +179,8 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   int piece_of[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    const int rr = c * kRowsPerLoad + lane / kPieces;   // row within the wave's 64
-    const int r = wid * 64 + rr;
+    const int rr = c * kRowsPerLoad + lane / kPieces;   // row within the wave's
+    const int r = rb + rr;
     piece_of[c] = (lane % kPieces) ^ ((r >> kSwzShift) & (kPieces - 1));
     const int64_t rw = min(w0 + rr, w_last) - wb;
     const int64_t rx = min(j0 + rr, a.rows - 1) - jb;
@@ -180,7 +190,7 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   // Operand units: unit u is operand u % 2 (0 weights, 1 tokens) of stage
   // u / 2, 256 rows of 128 bytes in LDS buffer u % kUnits.
   auto unit_lds = [&](int u) { return smem + (u % kUnits) * kUnitBytes; };
-  // load c (0 .. 7) of unit u, a full stage: a buffer load from the wave's
+  // load c (0 .. kChunks - 1) of unit u, a full stage: a buffer load from the wave's
   // first row (raw, unswizzled descriptor) with the lane offset in the VGPR and
   // the stage's K position in the scalar offset, so it takes no vector
   // arithmetic at all; lane offset plus K position stay below 128 K 2 <= 2^31,
@@ -195,7 +205,7 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (lds_void_ptr)dst, 16, w_off[c], kb2, 0, 0);
   };
-  // loads c0 .. 7 of unit u of any stage, the last one possibly past K:
+  // loads c0 .. kChunks - 1 of unit u of any stage, the last one possibly past K:
   // pieces past K read a zero piece
   auto load_unit = [&](int u, int c0) {
     const int64_t kb = (int64_t)(u >> 1) * kBK;
@@ -211,52 +221,53 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     }
   };
 
-  floatx16 acc[4][4];
+  floatx16 acc[4][kNT];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = floatx16{};
+    for (int n = 0; n < kNT; ++n) acc[m][n] = floatx16{};
 
   // fragment rows of this lane: weight rows wi*128 + m*32 + lane%32, token
-  // rows wj*128 + n*32 + lane%32, whose swizzle is that of lane%32 (the tile
+  // rows wj*kWaveTok + n*32 + lane%32, whose swizzle is that of lane%32 (the tile
   // offsets are multiples of the swizzle period)
   const int frow = lane & 31;
   const int fswz = (frow >> kSwzShift) & (kPieces - 1);
   const int nst = (int)((K + kBK - 1) / kBK);
   const int nst_full = (int)(K / kBK);   // stages entirely inside K
-  auto read_frags = [&](int st, int kk, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
+  auto read_frags = [&](int st, int kk, bf16x8 (&af)[4], bf16x8 (&bfr)[kNT]) {
     const uint8_t* wt = unit_lds(2 * st) + (wi * 128 + frow) * kRowBytes;
-    const uint8_t* xt = unit_lds(2 * st + 1) + (wj * 128 + frow) * kRowBytes;
+    const uint8_t* xt = unit_lds(2 * st + 1) + (wj * kWaveTok + frow) * kRowBytes;
     const int off = ((kk * 2 + half) ^ fswz) * 16;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
       af[m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wt + m * 32 * kRowBytes + off));
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < kNT; ++n)
       bfr[n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xt + n * 32 * kRowBytes + off));
   };
 
-  // Load sequence j: the 16 loads of units 2j + 5 (tokens of stage j + 2) and
+  // Load sequence j: the 2 kChunks loads of units 2j + 5 (tokens of stage j + 2) and
   // 2j + 6 (weights of stage j + 3), in that order.  Their buffers are those
   // of stage j's two units, free once every wave is past the barrier of
   // iteration j.
-  constexpr int kN3 = 8, kN0 = 4, kN1 = 4;       // loads per K-step (K-step 3, then 0, 1, 2)
+  constexpr int kN3 = kChunks, kN0 = kChunks / 2, kN1 = kChunks / 2;   // loads per K-step (3, then 0, 1, 2)
   constexpr int kN2 = 2 * kChunks - kN3 - kN0 - kN1;
   static_assert(kN3 <= kChunks && kN0 <= 8 && kN1 <= 8 && kN2 >= 0 && kN2 <= 8, "load spread");
-  auto load_seq = [&](int j, int p) { load_full(2 * j + 5 + (p >> 3), p & 7); };
+  auto load_seq = [&](int j, int p) { load_full(2 * j + 5 + p / kChunks, p % kChunks); };
   // the 16 MFMAs of one K-step: the first, then the other 15 with positions
   // p0 .. p0 + n - 1 of load sequence j spread between them (a load the
   // texture path cannot take yet stalls the wave, and the MFMAs behind it)
-  auto first_mfma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
+  auto first_mfma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[kNT]) {
     acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bfr[0], acc[0][0], 0, 0, 0);
   };
-  auto other_mfmas = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], int j, int p0, int n) {
+  auto other_mfmas = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[kNT], int j, int p0, int n) {
 #pragma unroll
-    for (int t = 1; t < 16; ++t) {
-      acc[t >> 2][t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t >> 2], bfr[t & 3], acc[t >> 2][t & 3], 0, 0, 0);
+    for (int t = 1; t < kTiles; ++t) {
+      acc[t / kNT][t % kNT] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t / kNT], bfr[t % kNT], acc[t / kNT][t % kNT], 0, 0, 0);
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        if (q < n && t == 1 + q * 15 / n) load_seq(j, p0 + q);
+        if (q < n && t == 1 + q * (kTiles - 1) / n) load_seq(j, p0 + q);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -268,6 +279,8 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
       wait_vmcnt<16>();
     else if (later >= 8)
       wait_vmcnt<8>();
+    else if (later >= 4)
+      wait_vmcnt<4>();
     else
       wait_vmcnt<0>();
     // lgkmcnt(0) + barrier, without the vmcnt(0) that a workgroup fence adds
@@ -282,10 +295,10 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   // stage st + 1 at a barrier.  Every read of a stage's units is issued before
   // that barrier and has completed at it (lgkmcnt(0)).
   // Steady state (all units involved full): iteration st issues positions
-  // kN3 .. 15 of sequence st - 1 in K-steps 0 .. 2 and positions 0 .. kN3 - 1
-  // of sequence st after its barrier, in K-step 3.  At the barrier, stage
-  // st + 1's tokens are positions 0 .. 7 of sequence st - 1, and the 8 loads
-  // issued after them may still be in flight.
+  // kN3 .. 2 kChunks - 1 of sequence st - 1 in K-steps 0 .. 2 and positions
+  // 0 .. kN3 - 1 of sequence st after its barrier, in K-step 3.  At the
+  // barrier, stage st + 1's tokens are positions 0 .. kChunks - 1 of sequence
+  // st - 1, and the kChunks loads issued after them may still be in flight.
   // Past the steady state, units are issued whole at the top of the iteration
   // (the last stage possibly partial), up to unit 2 st + 4, whose buffer was
   // freed at the barrier before.
@@ -300,12 +313,12 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     }
     return later;
   };
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  bf16x8 a0[4], b0[kNT], a1[4], b1[kNT];
   auto kstep = [&](int st, int kk, bool steady, int later) __attribute__((always_inline)) {
     bf16x8(&ca)[4] = (kk & 1) ? a1 : a0;
-    bf16x8(&cb)[4] = (kk & 1) ? b1 : b0;
+    bf16x8(&cb)[kNT] = (kk & 1) ? b1 : b0;
     bf16x8(&na)[4] = (kk & 1) ? a0 : a1;
-    bf16x8(&nb)[4] = (kk & 1) ? b0 : b1;
+    bf16x8(&nb)[kNT] = (kk & 1) ? b0 : b1;
     int j = 0, p0 = 0, n = 0;
     if (steady) {
       if (kk == kNK - 1) { j = st; p0 = 0; n = kN3; }
@@ -359,8 +372,8 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   // e % 4, token j = tj*256 + wj*128 + n*32 + lane % 32; four consecutive
   // output columns go out as one 8-byte store
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int64_t j = (int64_t)tj * kTileJ + wj * 128 + n * 32 + frow;
+  for (int n = 0; n < kNT; ++n) {
+    const int64_t j = (int64_t)tj * kTileJ + wj * kWaveTok + n * 32 + frow;
     if (j >= a.rows) continue;
     uint16_t* orow = a.out + j * a.n_out;
     if constexpr (kGateUp) {
