@@ -52,7 +52,8 @@ STRUCT_BLOCK = 64    # granularity of the generator's hot/cold structure
 # which bisects them against the oracle's keep ratio at p = 0.99).
 POWERLAW_C = 1.4590  # keeps 40.1% of the 2048 blocks of the 128K request at p = 0.99
 # hot-block alignment of each request of the varlen batch: the requests keep
-# 9.4%, 34.4%, 60.2% and 100% of their tokens (the last has only hot blocks)
+# 9.4%, 34.4%, 60.2% and 90.6% of their tokens (the last: 25 hot blocks of its
+# 28 non-forced ones, the 3 others dropped)
 HOT_LAMBDA_VARLEN = (8.0, 6.9462, 6.2224, 8.0)
 
 LLAMA_8B = dict(hq=32, hkv=8, d=128, hidden=4096)
@@ -349,7 +350,7 @@ def llama_varlen4(seed: int = 1, hot_lambda=None) -> Workload:
     """hot_lambda: one alignment for all four requests, or one per request."""
     lam = HOT_LAMBDA_VARLEN if hot_lambda is None else hot_lambda
     lams = tuple(lam) if isinstance(lam, (tuple, list)) else (float(lam),) * 4
-    hots = (2, 8, 20, 64)
+    hots = (2, 8, 20, 25)
     return Workload("llama8b_varlen4", (4096, 8192, 16384, 2048), seed=seed,
                     structures=tuple(RequestStructure("hot", hot=h, hot_lambda=l) for h, l in zip(hots, lams)),
                     **LLAMA_8B)

@@ -13,10 +13,11 @@ powerlaw: the power-law constant c of the 128K LLaMA-shaped workload (per-
 p = 0.99 (synth.POWERLAW_C).
 
 varlen: the hot-block alignment of each request of the 4-request varlen batch
-(lengths 4096 / 8192 / 16384 / 2048 with 2 / 8 / 20 / 64 hot blocks), so that
-the requests keep about 10%, 35% and 60% of their tokens; the 2048-token
-request has only 28 blocks that are neither sink nor window, all hot, and
-keeps every token whatever the alignment (synth.HOT_LAMBDA_VARLEN).  Each
+(lengths 4096 / 8192 / 16384 / 2048 with 2 / 8 / 20 / 25 hot blocks), so that
+the first three requests keep about 10%, 35% and 60% of their tokens; the
+2048-token request has 28 blocks that are neither sink nor window, 25 of them
+hot at alignment 8, and keeps 29 of its 32 blocks (90.6%) by construction
+(synth.HOT_LAMBDA_VARLEN).  Each
 request draws from its own streams, so its keep ratio depends on its own
 alignment only and the bisections are independent.
 """

@@ -22,4 +22,4 @@ def test_varlen_batch_keep_ratios_span_the_range():
     sel = oracle.select(q, k, cu, wl.hq, wl.hkv, wl.d, wl.G, wl.A, wl.n, wl.p)
     ratios = [int(sel["kept"][r]) / int(cu[r + 1] - cu[r]) for r in range(wl.num_reqs)]
     assert abs(ratios[0] - 0.10) < 0.02 and abs(ratios[1] - 0.35) < 0.03 and abs(ratios[2] - 0.60) < 0.03, ratios
-    assert ratios[3] == 1.0
+    assert abs(ratios[3] - 0.90) < 0.02, ratios
