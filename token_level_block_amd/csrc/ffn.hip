@@ -368,51 +368,58 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   }
   for (; st < nst; ++st) iteration(st, false);
 
-  // epilogue: element e of tile (m, n) is weight row i0 + 8 (e / 4) + 4 half +
-  // e % 4, token j = tj*256 + wj*128 + n*32 + lane % 32; four consecutive
-  // output columns go out as one 8-byte store
+  // Epilogue.  Element e of accumulator tile (m, n) is weight row (output
+  // column) wi*128 + m*32 + 8 (e / 4) + 4 half + e % 4 of the tile and token
+  // wj*kWaveTok + n*32 + lane % 32: a lane holds four runs of four columns of
+  // one token.  Stored as they are, every 8-byte piece of a store instruction
+  // lands in a different token row (64 cache lines per instruction), so the
+  // wave first writes its output block to LDS (token-major rows, free after
+  // the loop's last barrier: no wave reads the ring any more) and reads it
+  // back as 16-byte pieces of 8 columns, 8 (or 4) whole row segments per
+  // instruction.  16-byte pieces in an LDS row are XOR-swizzled by the token
+  // so that both the 8-byte writes and the 16-byte reads spread over the banks.
+  // Output widths are multiples of 8, so a 16-byte piece is wholly inside or
+  // wholly past the last column.
+  constexpr int kOutCols = kGateUp ? 64 : 128;        // output columns of a wave
+  constexpr int kOutPieces = kOutCols / 8;            // 16-byte pieces per token row
+  constexpr int kOutRowBytes = kOutCols * 2;
+  static_assert(kWaves * kWaveTok * kOutRowBytes <= kUnits * kUnitBytes, "epilogue blocks fit the LDS");
+  uint8_t* ob = smem + wid * (kWaveTok * kOutRowBytes);
+  auto out_at = [&](int t, int c) {   // byte offset of column c (a multiple of 4) of token t
+    return t * kOutRowBytes + (((c >> 3) ^ (t % kOutPieces)) << 4) + (c & 7) * 2;
+  };
 #pragma unroll
   for (int n = 0; n < kNT; ++n) {
-    const int64_t j = (int64_t)tj * kTileJ + wj * kWaveTok + n * 32 + frow;
-    if (j >= a.rows) continue;
-    uint16_t* orow = a.out + j * a.n_out;
-    if constexpr (kGateUp) {
+    const int t = n * 32 + frow;
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < (kGateUp ? 2 : 4); ++m) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t f = (int64_t)ti * 128 + wi * 64 + m * 32 + 8 * g + 4 * half;
-          bf16x4 o;
+      for (int g = 0; g < 4; ++g) {
+        const int c = m * 32 + 8 * g + 4 * half;
+        bf16x4 o;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) o[q] = (__bf16)(silu_f32(acc[m][n][4 * g + q]) * acc[m + 2][n][4 * g + q]);
-          if (f + 4 <= a.F) {
-            *reinterpret_cast<bf16x4*>(orow + f) = o;
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (f + q < a.F) reinterpret_cast<__bf16*>(orow)[f + q] = o[q];
-          }
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (kGateUp)
+            o[q] = (__bf16)(silu_f32(acc[m][n][4 * g + q]) * acc[m + 2][n][4 * g + q]);
+          else
+            o[q] = (__bf16)acc[m][n][4 * g + q];
         }
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t i = (int64_t)ti * kTileI + wi * 128 + m * 32 + 8 * g + 4 * half;
-          bf16x4 o;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) o[q] = (__bf16)acc[m][n][4 * g + q];
-          if (i + 4 <= a.n_out) {
-            *reinterpret_cast<bf16x4*>(orow + i) = o;
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (i + q < a.n_out) reinterpret_cast<__bf16*>(orow)[i + q] = o[q];
-          }
-        }
+        *reinterpret_cast<bf16x4*>(ob + out_at(t, c)) = o;
       }
     }
+  }
+  // first output column of the wave, and the row stride, in elements
+  const int64_t col0 = kGateUp ? (int64_t)ti * 128 + wi * 64 : (int64_t)ti * kTileI + wi * 128;
+  const int64_t ncols = kGateUp ? a.F : a.n_out;
+  constexpr int kTokPerRound = 64 / kOutPieces;   // token rows one 64-lane pass covers
+#pragma unroll
+  for (int r = 0; r < kWaveTok / kTokPerRound; ++r) {
+    const int t = r * kTokPerRound + lane / kOutPieces;
+    const int p = lane % kOutPieces;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ob + out_at(t, p * 8));
+    const int64_t j = (int64_t)tj * kTileJ + wj * kWaveTok + t;
+    const int64_t col = col0 + p * 8;
+    if (j < a.rows && col < ncols) *reinterpret_cast<u32x4*>(a.out + j * a.n_out + col) = v;
   }
 }
 
