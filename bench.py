@@ -710,6 +710,11 @@ def main():
         mfma_peak, copy_peak = measure_peaks(stream, ev)
         kv["frac"] = kv["write_gbs"] / PEAK_HBM_GBS
         kv["frac_measured"] = kv["write_gbs"] / copy_peak
+        # the FFN GEMMs against the dense bf16 peak and the measured MFMA rate
+        ffn.update(peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", bound="mfma",
+                   frac_full=ffn["tflops_full"] / PEAK_BF16_TFLOPS, frac_kept=ffn["tflops_kept"] / PEAK_BF16_TFLOPS,
+                   frac_measured_full=ffn["tflops_full"] / mfma_peak,
+                   frac_measured_kept=ffn["tflops_kept"] / mfma_peak)
         log(f"[bench] measured peaks: bf16 MFMA {mfma_peak:.0f} TFLOP/s (random operands), copy {copy_peak:.0f} GB/s")
     configs = None
     if not (args.step_only or args.no_configs):
