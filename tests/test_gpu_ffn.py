@@ -92,10 +92,12 @@ def check_rows(y_gpu, x_bits, wg_bits, wd_bits, where=""):
 
 
 # K = D or F: whole 64-element stages, a partial last stage (1000, 200, 584,
-# 136, 72, 1096), a single partial stage (8); weight panels fewer than 8
+# 136, 72, 1096), a single partial stage (8, 16, 24); the narrowest widths (D or
+# F = 8); a token tile past a multiple of 256 rows (257); weight panels fewer than 8
 # (one XCD walk) and 9 (the shared walk, split unevenly over the XCDs)
 @pytest.mark.parametrize("rows,D,F", [(300, 256, 512), (1, 64, 8), (77, 128, 1000), (513, 512, 1536),
-                                      (130, 200, 584), (64, 136, 72), (300, 2304, 1096)])
+                                      (130, 200, 584), (64, 136, 72), (300, 2304, 1096),
+                                      (5, 8, 16), (3, 16, 8), (257, 72, 24)])
 def test_ffn_small_shapes_all_rows(rows, D, F):
     rng_seed = rows + D + F
     wg = synth.uniform_bf16_bits(11 + rng_seed, 0, 2 * F, D, -4)
