@@ -121,26 +121,28 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   // Otherwise XCD x walks tiles [x T/8, (x+1) T/8) in order.  Either way the
   // workgroups of an XCD running together cover a few weight panels times
   // kGroupJ token panels, which they share in its L2.
+  // (32-bit arithmetic: the host keeps every tile count, and the grid, below 2^32)
   int ti, tj;
   {
-    const int x = blockIdx.x & 7;
-    const int64_t q = blockIdx.x >> 3;
-    int64_t wgi, grp, gj, ti0;
-    if (a.tiles_i >= 8) {
-      ti0 = (int64_t)x * a.tiles_i / 8;
-      const int64_t nti = (int64_t)(x + 1) * a.tiles_i / 8 - ti0;
-      if (q >= nti * a.tiles_j) return;
+    const uint32_t x = blockIdx.x & 7;
+    const uint32_t q = blockIdx.x >> 3;
+    const uint32_t tiles_i = (uint32_t)a.tiles_i, tiles_j = (uint32_t)a.tiles_j;
+    uint32_t wgi, grp, ti0;
+    if (tiles_i >= 8) {
+      ti0 = x * tiles_i / 8;
+      const uint32_t nti = (x + 1) * tiles_i / 8 - ti0;
+      if ((uint64_t)q >= (uint64_t)nti * tiles_j) return;
       grp = q / (nti * kGroupJ);
       wgi = q % (nti * kGroupJ);
     } else {
-      const int64_t ntiles = (int64_t)a.tiles_i * a.tiles_j;
-      const int64_t t = x * ((ntiles + 7) / 8) + q;
+      const uint32_t ntiles = tiles_i * tiles_j;
+      const uint32_t t = x * ((ntiles + 7) / 8) + q;
       if (t >= ntiles) return;
       ti0 = 0;
-      grp = t / ((int64_t)kGroupJ * a.tiles_i);
-      wgi = t % ((int64_t)kGroupJ * a.tiles_i);
+      grp = t / (kGroupJ * tiles_i);
+      wgi = t % (kGroupJ * tiles_i);
     }
-    gj = min((int64_t)kGroupJ, (int64_t)a.tiles_j - grp * kGroupJ);
+    const uint32_t gj = min((uint32_t)kGroupJ, tiles_j - grp * kGroupJ);
     ti = (int)(ti0 + wgi / gj);
     tj = (int)(grp * kGroupJ + wgi % gj);
   }
