@@ -12,10 +12,12 @@
 //      the registers);
 //   2. down: i over the D rows of Wd, j over the tokens, K = F; y as bf16.
 // A workgroup computes a 256 (weight rows) x 256 (tokens) tile with
-// v_mfma_f32_32x32x16_bf16: eight waves (two per SIMD, so that one wave's
+// v_mfma_f32_16x16x32_bf16: eight waves (two per SIMD, so that one wave's
 // stall on a load it cannot issue yet leaves the other issuing MFMAs) of
-// 128 x 64, each holding 4 x 2
-// accumulator tiles.  Operands stream through LDS with gfx950's direct
+// 128 x 64, each holding 8 x 4 accumulator tiles.  The part runs this kernel
+// at its power limit, and the 16 x 16 x 32 form moves half the accumulator
+// bytes per flop of the 32 x 32 x 16 one: the same loop with it holds a
+// clock about 12 % higher.  Operands stream through LDS with gfx950's direct
 // global-to-LDS 16-byte loads in stages of 64 K-elements: a row's 128 bytes
 // per stage make whole 128-byte L2 requests (64-byte rows took twice the
 // requests, and the L1-to-L2 path is what bounds the kernel).  The 160 KB of
@@ -23,13 +25,14 @@
 // 32 KB each), so the loads of a unit are issued one to two stages before it
 // is read, spread between the MFMAs (a burst stalls the waves at the texture
 // unit); they are buffer loads whose only per-stage change is a scalar
-// offset.  The next K-step's fragments are read while the current one's MFMAs
-// run, and the one barrier per stage waits only for the stage it needs.
-// Pieces are XOR-swizzled by (row / 2) & 7, so the 16 lanes of each pass of a
-// fragment read hit 16 different bank groups.
+// offset.  The next K-step's fragments are read one at a time between the
+// current one's MFMAs, and the one barrier per stage waits only for the stage
+// it needs.
+// Pieces are XOR-swizzled by (row / 2) & 7, so the 16 rows of a fragment read
+// hit 16 different bank groups.
 // In the gate/up launch the workgroup's 256 weight rows are 64 gate rows, the
 // 64 up rows of the same channels, then the next 64 of each: a wave's first
-// two accumulator rows of tiles are gate and its last two the matching up
+// four accumulator rows of tiles are gate and its last four the matching up
 // channels, so gate and up of one (token, channel) sit in the same lane and
 // register.  Rows past the end are clamped (their results are not stored) and
 // K past the end reads a zero piece.  The tile walk shares token panels
@@ -42,7 +45,7 @@ namespace up {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;                 // two per SIMD
@@ -52,17 +55,18 @@ constexpr int kTileJ = 256;               // tokens per workgroup
 constexpr int kBK = 64;                   // K elements per stage
 constexpr int kRowBytes = kBK * 2;        // one row's bytes in a stage (128)
 constexpr int kPieces = kRowBytes / 16;   // 16-byte pieces per row (8)
-constexpr int kNK = kBK / 16;             // MFMA K-steps per stage (4)
+constexpr int kNK = kBK / 32;             // MFMA K-steps per stage (2)
 constexpr int kUnitBytes = 256 * kRowBytes;   // one operand's 256 rows of a stage (32 KB)
 constexpr int kUnits = 5;                 // LDS ring of operand units (160 KB)
 constexpr int kRowsPerLoad = 1024 / kRowBytes;   // rows one 1 KB wave load covers (8)
 constexpr int kWaveRows = 256 / kWaves;         // rows of each unit one wave loads
 constexpr int kChunks = kWaveRows / kRowsPerLoad;  // loads per operand per wave per stage
-// wave tile: 128 weight rows (4 MFMA tiles) x kWaveTok tokens (kNT tiles)
+// wave tile: 128 weight rows (kMT MFMA tiles of 16) x kWaveTok tokens (kNT tiles of 16)
 constexpr int kWaveTok = kTileJ / (kWaves / 2);
-constexpr int kNT = kWaveTok / 32;
-constexpr int kTiles = 4 * kNT;                    // MFMAs per K-step per wave
-static_assert(kWaves == 4 || kWaves == 8, "wave layouts");
+constexpr int kMT = 128 / 16;
+constexpr int kNT = kWaveTok / 16;
+constexpr int kTiles = kMT * kNT;                  // MFMAs per K-step per wave (32)
+static_assert(kWaves == 8 && kNK == 2, "wave layout and K-step schedule");
 // LDS pieces are XOR-swizzled by (row / 2) & 7: the 16 rows that share a
 // 256-byte window of banks get distinct pieces
 constexpr int kSwzShift = 1;
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wi = wid / (kWaves / 2), wj = wid % (kWaves / 2);
-  const int half = lane >> 5;
+  const int quad = lane >> 4;
 
   // tile of this workgroup.  Workgroups are dealt to the 8 XCDs round-robin
   // (XCD x = id mod 8 runs the ones with id / 8 = 0, 1, 2, ... in turn).
@@ -223,56 +227,40 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     }
   };
 
-  floatx16 acc[4][kNT];
+  floatx4 acc[kMT][kNT];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < kMT; ++m)
 #pragma unroll
-    for (int n = 0; n < kNT; ++n) acc[m][n] = floatx16{};
+    for (int n = 0; n < kNT; ++n) acc[m][n] = floatx4{};
 
-  // fragment rows of this lane: weight rows wi*128 + m*32 + lane%32, token
-  // rows wj*kWaveTok + n*32 + lane%32, whose swizzle is that of lane%32 (the tile
-  // offsets are multiples of the swizzle period)
-  const int frow = lane & 31;
+  // fragment f of a K-step (A tiles 0 .. kMT - 1, then B tiles): lane rows
+  // weight wi*128 + 16 f + lane%16 or token wj*kWaveTok + 16 (f - kMT) + lane%16,
+  // 16-byte piece 4 kk + lane/16 of the stage's 128-byte row; the swizzle is
+  // that of lane%16 (the tile offsets are multiples of the swizzle period)
+  const int frow = lane & 15;
   const int fswz = (frow >> kSwzShift) & (kPieces - 1);
   const int nst = (int)((K + kBK - 1) / kBK);
   const int nst_full = (int)(K / kBK);   // stages entirely inside K
-  auto read_frags = [&](int st, int kk, bf16x8 (&af)[4], bf16x8 (&bfr)[kNT]) {
-    const uint8_t* wt = unit_lds(2 * st) + (wi * 128 + frow) * kRowBytes;
-    const uint8_t* xt = unit_lds(2 * st + 1) + (wj * kWaveTok + frow) * kRowBytes;
-    const int off = ((kk * 2 + half) ^ fswz) * 16;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      af[m] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wt + m * 32 * kRowBytes + off));
-#pragma unroll
-    for (int n = 0; n < kNT; ++n)
-      bfr[n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xt + n * 32 * kRowBytes + off));
+  constexpr int kFrags = kMT + kNT;
+  auto read_frag = [&](int st, int kk, int f, bf16x8 (&af)[kMT], bf16x8 (&bfr)[kNT]) {
+    const int off = ((kk * 4 + quad) ^ fswz) * 16;
+    if (f < kMT) {
+      const uint8_t* wt = unit_lds(2 * st) + (wi * 128 + f * 16 + frow) * kRowBytes;
+      af[f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wt + off));
+    } else {
+      const uint8_t* xt = unit_lds(2 * st + 1) + (wj * kWaveTok + (f - kMT) * 16 + frow) * kRowBytes;
+      bfr[f - kMT] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xt + off));
+    }
   };
 
   // Load sequence j: the 2 kChunks loads of units 2j + 5 (tokens of stage j + 2) and
   // 2j + 6 (weights of stage j + 3), in that order.  Their buffers are those
   // of stage j's two units, free once every wave is past the barrier of
-  // iteration j.
-  constexpr int kN3 = kChunks, kN0 = kChunks / 2, kN1 = kChunks / 2;   // loads per K-step (3, then 0, 1, 2)
-  constexpr int kN2 = 2 * kChunks - kN3 - kN0 - kN1;
-  static_assert(kN3 <= kChunks && kN0 <= 8 && kN1 <= 8 && kN2 >= 0 && kN2 <= 8, "load spread");
+  // iteration j.  The tokens go out in the K-step after that barrier, the
+  // weights in the first K-step of iteration j + 1.
+  constexpr int kN1 = kChunks, kN0 = kChunks;   // loads in K-step 1, K-step 0
+  static_assert(kN1 + kN0 == 2 * kChunks && kN0 <= 8 && kN1 <= 8, "load spread");
   auto load_seq = [&](int j, int p) { load_full(2 * j + 5 + p / kChunks, p % kChunks); };
-  // the 16 MFMAs of one K-step: the first, then the other 15 with positions
-  // p0 .. p0 + n - 1 of load sequence j spread between them (a load the
-  // texture path cannot take yet stalls the wave, and the MFMAs behind it)
-  auto first_mfma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[kNT]) {
-    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bfr[0], acc[0][0], 0, 0, 0);
-  };
-  auto other_mfmas = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[kNT], int j, int p0, int n) {
-#pragma unroll
-    for (int t = 1; t < kTiles; ++t) {
-      acc[t / kNT][t % kNT] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t / kNT], bfr[t % kNT], acc[t / kNT][t % kNT], 0, 0, 0);
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (q < n && t == 1 + q * (kTiles - 1) / n) load_seq(j, p0 + q);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
   // wait until a stage has landed, given the number of loads issued after its
   // last one (loads complete in issue order), then make every wave's loads
   // visible and every wave's earlier LDS reads complete
@@ -291,14 +279,15 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     asm volatile("s_barrier" ::: "memory");
   };
 
-  // Iteration st computes stage st, K-step by K-step: the first MFMA, the
-  // reads of the next K-step's fragments, the other 15 MFMAs; before the last
-  // K-step's reads (those of stage st + 1's first K-step) the wave waits for
-  // stage st + 1 at a barrier.  Every read of a stage's units is issued before
-  // that barrier and has completed at it (lgkmcnt(0)).
+  // Iteration st computes stage st, K-step by K-step: 32 MFMAs, the first
+  // kFrags of them each followed by one read of the next K-step's fragments;
+  // before the last K-step (whose reads are those of stage st + 1's first
+  // K-step) the wave waits for stage st + 1 at a barrier.  Every read of a
+  // stage's units is issued before that barrier and has completed at it
+  // (lgkmcnt(0)).
   // Steady state (all units involved full): iteration st issues positions
-  // kN3 .. 2 kChunks - 1 of sequence st - 1 in K-steps 0 .. 2 and positions
-  // 0 .. kN3 - 1 of sequence st after its barrier, in K-step 3.  At the
+  // kN1 .. 2 kChunks - 1 of sequence st - 1 in K-step 0 and positions
+  // 0 .. kN1 - 1 of sequence st after its barrier, in K-step 1.  At the
   // barrier, stage st + 1's tokens are positions 0 .. kChunks - 1 of sequence
   // st - 1, and the kChunks loads issued after them may still be in flight.
   // Past the steady state, units are issued whole at the top of the iteration
@@ -315,33 +304,35 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     }
     return later;
   };
-  bf16x8 a0[4], b0[kNT], a1[4], b1[kNT];
+  bf16x8 a0[kMT], b0[kNT], a1[kMT], b1[kNT];
   auto kstep = [&](int st, int kk, bool steady, int later) __attribute__((always_inline)) {
-    bf16x8(&ca)[4] = (kk & 1) ? a1 : a0;
+    bf16x8(&ca)[kMT] = (kk & 1) ? a1 : a0;
     bf16x8(&cb)[kNT] = (kk & 1) ? b1 : b0;
-    bf16x8(&na)[4] = (kk & 1) ? a0 : a1;
+    bf16x8(&na)[kMT] = (kk & 1) ? a0 : a1;
     bf16x8(&nb)[kNT] = (kk & 1) ? b0 : b1;
     int j = 0, p0 = 0, n = 0;
     if (steady) {
-      if (kk == kNK - 1) { j = st; p0 = 0; n = kN3; }
-      else if (kk == 0) { j = st - 1; p0 = kN3; n = kN0; }
-      else if (kk == 1) { j = st - 1; p0 = kN3 + kN0; n = kN1; }
-      else { j = st - 1; p0 = kN3 + kN0 + kN1; n = kN2; }
+      if (kk == kNK - 1) { j = st; p0 = 0; n = kN1; }
+      else { j = st - 1; p0 = kN1; n = kN0; }
     }
-    if (kk < kNK - 1) {
-      first_mfma(ca, cb);
+    // the next K-step: this stage's second, or stage st + 1's first (in the
+    // last stage the wave waits for everything and reads units it never uses)
+    const int rst = (kk < kNK - 1) ? st : st + 1;
+    const int rkk = (kk < kNK - 1) ? kk + 1 : 0;
+    if (kk == kNK - 1) stage_landed(later);
+    // MFMA t, then fragment read t, with positions p0 .. p0 + n - 1 of load
+    // sequence j spread over the K-step (a load the texture path cannot take
+    // yet stalls the wave, and the MFMAs behind it)
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      acc[t / kNT][t % kNT] =
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[t / kNT], cb[t % kNT], acc[t / kNT][t % kNT], 0, 0, 0);
+      if (t < kFrags) read_frag(rst, rkk, t, na, nb);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < n && t == 1 + q * (kTiles - 1) / n) load_seq(j, p0 + q);
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(st, kk + 1, na, nb);
-    } else {
-      // in the last stage this waits for everything and reads units it never uses
-      stage_landed(later);
-      first_mfma(ca, cb);
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(st + 1, 0, na, nb);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    other_mfmas(ca, cb, j, p0, n);
-    __builtin_amdgcn_sched_barrier(0);
   };
   auto iteration = [&](int st, bool steady) __attribute__((always_inline)) {
     const int later = steady ? kChunks : top_up(st);
@@ -357,23 +348,24 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   int pro_later = top_up(-1);
   if (steady_end > 0) {
 #pragma unroll
-    for (int p = 0; p < kN3; ++p) load_seq(-1, p);
-    pro_later += kN3;
+    for (int p = 0; p < kN1; ++p) load_seq(-1, p);
+    pro_later += kN1;
   }
   stage_landed(pro_later);
-  read_frags(0, 0, a0, b0);
+#pragma unroll
+  for (int f = 0; f < kFrags; ++f) read_frag(0, 0, f, a0, b0);
   int st = 0;
   for (; st < steady_end; ++st) iteration(st, true);
   if (steady_end > 0) {   // sequence steady_end - 1 was begun
     next_unit = 2 * steady_end + 3;
-    partial = kN3;
+    partial = kN1;
   }
   for (; st < nst; ++st) iteration(st, false);
 
   // Epilogue.  Element e of accumulator tile (m, n) is weight row (output
-  // column) wi*128 + m*32 + 8 (e / 4) + 4 half + e % 4 of the tile and token
-  // wj*kWaveTok + n*32 + lane % 32: a lane holds four runs of four columns of
-  // one token.  Stored as they are, every 8-byte piece of a store instruction
+  // column) wi*128 + m*16 + 4 (lane / 16) + e of the tile and token
+  // wj*kWaveTok + n*16 + lane % 16: a lane holds runs of four columns of one
+  // token.  Stored as they are, every 8-byte piece of a store instruction
   // lands in a different token row (64 cache lines per instruction), so the
   // wave first writes its output block to LDS (token-major rows, free after
   // the loop's last barrier: no wave reads the ring any more) and reads it
@@ -392,22 +384,19 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   };
 #pragma unroll
   for (int n = 0; n < kNT; ++n) {
-    const int t = n * 32 + frow;
+    const int t = n * 16 + frow;
 #pragma unroll
-    for (int m = 0; m < (kGateUp ? 2 : 4); ++m) {
+    for (int m = 0; m < (kGateUp ? kMT / 2 : kMT); ++m) {
+      const int c = m * 16 + 4 * quad;
+      bf16x4 o;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = m * 32 + 8 * g + 4 * half;
-        bf16x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if constexpr (kGateUp)
-            o[q] = (__bf16)(silu_f32(acc[m][n][4 * g + q]) * acc[m + 2][n][4 * g + q]);
-          else
-            o[q] = (__bf16)acc[m][n][4 * g + q];
-        }
-        *reinterpret_cast<bf16x4*>(ob + out_at(t, c)) = o;
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (kGateUp)
+          o[q] = (__bf16)(silu_f32(acc[m][n][q]) * acc[m + kMT / 2][n][q]);
+        else
+          o[q] = (__bf16)acc[m][n][q];
       }
+      *reinterpret_cast<bf16x4*>(ob + out_at(t, c)) = o;
     }
   }
   // first output column of the wave, and the row stride, in elements
