@@ -109,6 +109,11 @@ constexpr int kRawBufferFlags = 0x00020000;
 // host-side launch stub)
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+// rows of the XCD grid of the tile walk (8, 4 or 2) for tiles_i >= 8 weight panels
+__host__ __device__ constexpr uint32_t ffn_xcd_rows(uint32_t tiles_i) {
+  return tiles_i >= 32 ? 8u : (tiles_i >= 16 ? 4u : 2u);
+}
+
 template <bool kGateUp>
 __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kUnits * kUnitBytes];
@@ -119,12 +124,15 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
 
   // tile of this workgroup.  Workgroups are dealt to the 8 XCDs round-robin
   // (XCD x = id mod 8 runs the ones with id / 8 = 0, 1, 2, ... in turn).
-  // With 8 or more weight panels, every XCD walks the same run of kGroupJ
-  // token panels at once, over its own eighth of the weight panels: a token
-  // panel leaves HBM once and the other XCDs' L2 misses on it hit the MALL.
-  // Otherwise XCD x walks tiles [x T/8, (x+1) T/8) in order.  Either way the
-  // workgroups of an XCD running together cover a few weight panels times
-  // kGroupJ token panels, which they share in its L2.
+  // With 8 or more weight panels the XCDs form an xi x (8 / xi) grid: XCD x
+  // takes the (x mod xi)-th of xi equal runs of weight panels and every
+  // (8 / xi)-th group of kGroupJ token panels, starting at group x / xi, and
+  // walks them group by group.  The 32 workgroups an XCD runs together then
+  // cover at least 4 weight panels times a group of token panels (xi is the
+  // largest of 8, 4, 2 that leaves each XCD 4 weight panels or more), which
+  // they share in its L2; the XCDs of one column walk the same token groups
+  // at once, so a token panel leaves HBM once and their other L2 misses on it
+  // hit the MALL.  Otherwise XCD x walks tiles [x T/8, (x+1) T/8) in order.
   // (32-bit arithmetic: the host keeps every tile count, and the grid, below 2^32)
   int ti, tj;
   {
@@ -133,11 +141,13 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     const uint32_t tiles_i = (uint32_t)a.tiles_i, tiles_j = (uint32_t)a.tiles_j;
     uint32_t wgi, grp, ti0;
     if (tiles_i >= 8) {
-      ti0 = x * tiles_i / 8;
-      const uint32_t nti = (x + 1) * tiles_i / 8 - ti0;
-      if ((uint64_t)q >= (uint64_t)nti * tiles_j) return;
-      grp = q / (nti * kGroupJ);
+      const uint32_t xi = ffn_xcd_rows(tiles_i), xj = 8 / xi;
+      const uint32_t gi = x % xi;
+      ti0 = gi * tiles_i / xi;
+      const uint32_t nti = (gi + 1) * tiles_i / xi - ti0;
+      grp = (q / (nti * kGroupJ)) * xj + x / xi;
       wgi = q % (nti * kGroupJ);
+      if (grp * kGroupJ >= tiles_j || wgi >= nti * min((uint32_t)kGroupJ, tiles_j - grp * kGroupJ)) return;
     } else {
       const uint32_t ntiles = tiles_i * tiles_j;
       const uint32_t t = x * ((ntiles + 7) / 8) + q;
@@ -414,9 +424,13 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   }
 }
 
-// workgroups the kernel's tile walk takes
+// workgroups the kernel's tile walk takes: 8 times the most tiles any XCD
+// can get (ids past an XCD's share exit at once)
 int64_t ffn_gemm_grid(int64_t tiles_i, int64_t tiles_j) {
-  return tiles_i >= 8 ? 8 * ((tiles_i + 7) / 8) * tiles_j : (tiles_i * tiles_j + 7) / 8 * 8;
+  if (tiles_i < 8) return (tiles_i * tiles_j + 7) / 8 * 8;
+  const int64_t xi = ffn_xcd_rows((uint32_t)(tiles_i < 32 ? tiles_i : 32)), xj = 8 / xi;
+  const int64_t groups = (tiles_j + kGroupJ - 1) / kGroupJ;
+  return 8 * ((tiles_i + xi - 1) / xi) * kGroupJ * ((groups + xj - 1) / xj);
 }
 
 static hipError_t launch_ffn_gemm(bool gate_up, const FfnGemmArgs& a, hipStream_t s) {
