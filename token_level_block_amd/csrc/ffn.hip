@@ -203,8 +203,14 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     w_off[c] = (uint32_t)(rw * K * 2 + piece_of[c] * 16);
     x_off[c] = (uint32_t)(rx * K * 2 + piece_of[c] * 16);
   }
-  // Operand units: unit u is operand u % 2 (0 weights, 1 tokens) of stage
-  // u / 2, 256 rows of 128 bytes in LDS buffer u % kUnits.
+  // Operand units: unit u holds one operand of stage u / 2, 256 rows of 128
+  // bytes in LDS buffer u % kUnits; the weights are the units of parity kWUnit.
+  // The load schedule below gives even units the longer lead, so it goes to
+  // the operand whose L2 misses go further: in the gate/up launch the weights
+  // (every XCD walks its own weight panels, 235 MB between them for LLaMA-8B
+  // widths), in the down launch the tokens (the activation h streams from
+  // HBM, while the 117 MB of Wd stay in the MALL).
+  constexpr int kWUnit = kGateUp ? 0 : 1;
   auto unit_lds = [&](int u) { return smem + (u % kUnits) * kUnitBytes; };
   // load c (0 .. kChunks - 1) of unit u, a full stage: a buffer load from the wave's
   // first row (raw, unswizzled descriptor) with the lane offset in the VGPR and
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   auto load_full = [&](int u, int c) {
     const int kb2 = (u >> 1) * (2 * kBK);
     uint8_t* dst = unit_lds(u) + (wid * kChunks + c) * 1024;
-    if (u & 1)
+    if ((u & 1) != kWUnit)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_x, (lds_void_ptr)dst, 16, x_off[c], kb2, 0, 0);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (lds_void_ptr)dst, 16, w_off[c], kb2, 0, 0);
@@ -226,12 +232,13 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   auto load_unit = [&](int u, int c0) {
     const int64_t kb = (int64_t)(u >> 1) * kBK;
     const bool full = kb + kBK <= K;
-    const uint8_t* base = (u & 1) ? wave_x : wave_w;
+    const bool tok = (u & 1) != kWUnit;
+    const uint8_t* base = tok ? wave_x : wave_w;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       if (c < c0) continue;
       const bool in_k = full || kb + piece_of[c] * 8 < K;
-      const uint8_t* g = base + ((u & 1) ? x_off[c] : w_off[c]) + kb * 2;
+      const uint8_t* g = base + (tok ? x_off[c] : w_off[c]) + kb * 2;
       __builtin_amdgcn_global_load_lds(in_k ? (const void*)g : (const void*)kZeroPiece,
                                        (lds_void_ptr)(unit_lds(u) + (wid * kChunks + c) * 1024), 16, 0, 0);
     }
@@ -252,22 +259,24 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   const int nst = (int)((K + kBK - 1) / kBK);
   const int nst_full = (int)(K / kBK);   // stages entirely inside K
   constexpr int kFrags = kMT + kNT;
+  static_assert(kMT == 8 && kNT == 4 && (kFrags - 1) * 8 / 3 < kTiles, "read schedule");
   auto read_frag = [&](int st, int kk, int f, bf16x8 (&af)[kMT], bf16x8 (&bfr)[kNT]) {
     const int off = ((kk * 4 + quad) ^ fswz) * 16;
     if (f < kMT) {
-      const uint8_t* wt = unit_lds(2 * st) + (wi * 128 + f * 16 + frow) * kRowBytes;
+      const uint8_t* wt = unit_lds(2 * st + kWUnit) + (wi * 128 + f * 16 + frow) * kRowBytes;
       af[f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(wt + off));
     } else {
-      const uint8_t* xt = unit_lds(2 * st + 1) + (wj * kWaveTok + (f - kMT) * 16 + frow) * kRowBytes;
+      const uint8_t* xt = unit_lds(2 * st + 1 - kWUnit) + (wj * kWaveTok + (f - kMT) * 16 + frow) * kRowBytes;
       bfr[f - kMT] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xt + off));
     }
   };
 
-  // Load sequence j: the 2 kChunks loads of units 2j + 5 (tokens of stage j + 2) and
-  // 2j + 6 (weights of stage j + 3), in that order.  Their buffers are those
-  // of stage j's two units, free once every wave is past the barrier of
-  // iteration j.  The tokens go out in the K-step after that barrier, the
-  // weights in the first K-step of iteration j + 1.
+  // Load sequence j: the 2 kChunks loads of units 2j + 5 (the odd unit of
+  // stage j + 2) and 2j + 6 (the even unit of stage j + 3), in that order.
+  // Their buffers are those of stage j's two units, free once every wave is
+  // past the barrier of iteration j.  The first go out in the K-step after that
+  // barrier (one stage ahead of their use), the second in the first K-step of
+  // iteration j + 1 (one and a half stages ahead).
   constexpr int kN1 = kChunks, kN0 = kChunks;   // loads in K-step 1, K-step 0
   static_assert(kN1 + kN0 == 2 * kChunks && kN0 <= 8 && kN1 <= 8, "load spread");
   auto load_seq = [&](int j, int p) { load_full(2 * j + 5 + p / kChunks, p % kChunks); };
@@ -289,9 +298,8 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     asm volatile("s_barrier" ::: "memory");
   };
 
-  // Iteration st computes stage st, K-step by K-step: 32 MFMAs, the first
-  // kFrags of them each followed by one read of the next K-step's fragments;
-  // before the last K-step (whose reads are those of stage st + 1's first
+  // Iteration st computes stage st, K-step by K-step: 32 MFMAs with the reads
+  // of the next K-step's fragments spread between them; before the last K-step (whose reads are those of stage st + 1's first
   // K-step) the wave waits for stage st + 1 at a barrier.  Every read of a
   // stage's units is issued before that barrier and has completed at it
   // (lgkmcnt(0)).
@@ -330,14 +338,22 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     const int rst = (kk < kNK - 1) ? st : st + 1;
     const int rkk = (kk < kNK - 1) ? kk + 1 : 0;
     if (kk == kNK - 1) stage_landed(later);
-    // MFMA t, then fragment read t, with positions p0 .. p0 + n - 1 of load
-    // sequence j spread over the K-step (a load the texture path cannot take
-    // yet stalls the wave, and the MFMAs behind it)
+    // MFMA t, then the reads and loads of its slot: the next K-step's
+    // fragments one every 8/3 slots, in the order the next K-step first uses
+    // them (B0, A0, B1, B2, B3, A1 .. A7: each at least 23 slots ahead of its
+    // use), and positions p0 .. p0 + n - 1 of load sequence j spread over the
+    // K-step (a load the texture path cannot take yet stalls the wave, and
+    // the MFMAs behind it).  The MFMA stays ahead of its slot's read: a read
+    // issued first would make the wait for the previous K-step's fragments,
+    // at the top of the stage loop, wait for it too.
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       acc[t / kNT][t % kNT] =
           __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[t / kNT], cb[t % kNT], acc[t / kNT][t % kNT], 0, 0, 0);
-      if (t < kFrags) read_frag(rst, rkk, t, na, nb);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kFrags; ++i)
+        if (t == (i * 8) / 3) read_frag(rst, rkk, i == 0 ? kMT : (i == 1 ? 0 : (i <= kNT ? kMT + i - 1 : i - kNT)), na, nb);
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         if (q < n && t == 1 + q * (kTiles - 1) / n) load_seq(j, p0 + q);
@@ -353,7 +369,7 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   // iterations 0 .. steady_end - 1 are steady: sequences -1 .. steady_end - 1
   // are of full units
   const int steady_end = max(0, nst_full - 3);
-  // prologue: stage 0 and the weights of stage 1, then (when iteration 0 is
+  // prologue: stage 0 and the even unit of stage 1, then (when iteration 0 is
   // steady) the first positions of sequence -1, as iteration -1 would have
   int pro_later = top_up(-1);
   if (steady_end > 0) {
