@@ -115,8 +115,9 @@ def measured_traffic(root):
 
 def measure_peaks(stream, ev):
     """Rates this GPU sustains, from libuppeaks: dense bf16 MFMA on random
-    operands (TFLOP/s) and a streaming 1 GiB device copy (GB/s, read + write).
-    Best of three launches after one warm-up each."""
+    operands with the 32x32x16 instruction (the score kernel's) and the
+    16x16x32 one (the FFN GEMM's), in TFLOP/s, and a streaming 1 GiB device
+    copy (GB/s, read + write).  Best of three launches after one warm-up each."""
     import torch
     lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                    "token_level_block_amd", "libuppeaks.so"))
@@ -125,6 +126,7 @@ def measure_peaks(stream, ev):
     lib.upk_mfma_flops.restype = ctypes.c_double
     lib.upk_mfma_flops.argtypes = [ctypes.c_int32]
     lib.upk_mfma_launch.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    lib.upk_mfma16_launch.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     lib.upk_copy_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                     ctypes.c_void_p]
 
@@ -143,6 +145,7 @@ def measure_peaks(stream, ev):
     blocks = 256 * 8
     out = torch.empty(lib.upk_mfma_out_floats(blocks), dtype=torch.float32, device="cuda")
     mfma = best(lambda: lib.upk_mfma_launch(out.data_ptr(), blocks, stream), lib.upk_mfma_flops(blocks)) / 1e12
+    mfma16 = best(lambda: lib.upk_mfma16_launch(out.data_ptr(), blocks, stream), lib.upk_mfma_flops(blocks)) / 1e12
     nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -150,7 +153,7 @@ def measure_peaks(stream, ev):
                 2.0 * nbytes) / 1e9
     torch.cuda.synchronize()
     del out, src, dst
-    return mfma, copy
+    return mfma, mfma16, copy
 
 
 def time_kv_cache(cu_out, seq_lens, R, kept, wl, stream, ev, reps, B=16):
@@ -238,7 +241,7 @@ def time_ffn(keep_mask, cu_d, R, T, kept, wl, stream, ev, reps=3):
             "ms_full": ms_full, "ms_kept": ms_kept,
             "tflops_full": flops(T) / (ms_full * 1e-3) / 1e12, "tflops_kept": flops(kept) / (ms_kept * 1e-3) / 1e12,
             "saving_measured": 1.0 - ms_kept / ms_full, "saving_eq10": 1.0 - kept / T,
-            "gemms": "ffn_gemm_kernel: bf16 MFMA 32x32x16, fp32 accumulate; SwiGLU fused into the gate/up epilogue"}
+            "gemms": "ffn_gemm_kernel: bf16 MFMA 16x16x32, fp32 accumulate; SwiGLU fused into the gate/up epilogue"}
 
 
 def ratio(a, b):
@@ -696,7 +699,7 @@ def main():
     all_gbs = (sc_bytes + qk_bytes) / ((select_ms + compact_ms) * 1e-3) / 1e9
     torch.cuda.empty_cache()
     kv = ffn = None
-    mfma_peak = copy_peak = None
+    mfma_peak = mfma16_peak = copy_peak = None
     if not args.step_only:
         # the timed steps re-applied the same drop, so take the patched lengths of a
         # single drop on a fresh prefill: the retained counts
@@ -707,15 +710,18 @@ def main():
         ffn = time_ffn(sel.keep_mask, cu_d, R, T, kept, wl, stream, ev)
         log(f"[bench] FFN on {kept} retained rows {ffn['ms_kept']:.2f} ms vs {T} rows {ffn['ms_full']:.2f} ms: "
             f"saving {ffn['saving_measured']:.3f} (Eq. 10: {ffn['saving_eq10']:.3f})")
-        mfma_peak, copy_peak = measure_peaks(stream, ev)
+        mfma_peak, mfma16_peak, copy_peak = measure_peaks(stream, ev)
         kv["frac"] = kv["write_gbs"] / PEAK_HBM_GBS
         kv["frac_measured"] = kv["write_gbs"] / copy_peak
-        # the FFN GEMMs against the dense bf16 peak and the measured MFMA rate
+        # the FFN GEMMs against the dense bf16 peak and the measured rate of
+        # their own instruction (16x16x32)
         ffn.update(peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", bound="mfma",
                    frac_full=ffn["tflops_full"] / PEAK_BF16_TFLOPS, frac_kept=ffn["tflops_kept"] / PEAK_BF16_TFLOPS,
-                   frac_measured_full=ffn["tflops_full"] / mfma_peak,
-                   frac_measured_kept=ffn["tflops_kept"] / mfma_peak)
-        log(f"[bench] measured peaks: bf16 MFMA {mfma_peak:.0f} TFLOP/s (random operands), copy {copy_peak:.0f} GB/s")
+                   measured_peak=mfma16_peak,
+                   frac_measured_full=ffn["tflops_full"] / mfma16_peak,
+                   frac_measured_kept=ffn["tflops_kept"] / mfma16_peak)
+        log(f"[bench] measured peaks: bf16 MFMA {mfma_peak:.0f} TFLOP/s (32x32x16) and {mfma16_peak:.0f} TFLOP/s "
+            f"(16x16x32), random operands; copy {copy_peak:.0f} GB/s")
     configs = None
     if not (args.step_only or args.no_configs):
         configs = run_configs(args.steps, args.warmup, ev, stream)
@@ -777,8 +783,9 @@ def main():
                                           "over": "all of select + compact, K and window-query reads included"},
         "kv_cache_eq16": kv,
         "ffn_eq7": ffn,
-        "measured_peaks": {"bf16_mfma_tflops": mfma_peak, "copy_gbs": copy_peak,
-                           "how": "libuppeaks: random-operand 32x32x16 bf16 MFMA loop at 2 waves/SIMD; "
+        "measured_peaks": {"bf16_mfma_tflops": mfma_peak, "bf16_mfma16_tflops": mfma16_peak, "copy_gbs": copy_peak,
+                           "how": "libuppeaks: random-operand bf16 MFMA loops at 2 waves/SIMD, "
+                                  "32x32x16 (bf16_mfma_tflops) and 16x16x32 (bf16_mfma16_tflops); "
                                   "1 GiB streaming copy, one 16-byte unit per thread in one pass, "
                                   "read + write bytes"},
         "ms_per_step_mall_flushed": m["ms_flushed"],

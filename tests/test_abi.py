@@ -205,10 +205,11 @@ def test_single_hip_runtime_in_process():
 
 def test_peaks_library_exports_and_rejects():
     """libuppeaks (the benchmark's reference-rate probes) loads, exports its
-    four calls, and rejects bad arguments before launching anything."""
+    five calls, and rejects bad arguments before launching anything."""
     path = os.path.join(os.path.dirname(tlb.LIB_PATH), "libuppeaks.so")
     lib = ctypes.CDLL(path)
-    for name in ("upk_mfma_out_floats", "upk_mfma_flops", "upk_mfma_launch", "upk_copy_launch"):
+    for name in ("upk_mfma_out_floats", "upk_mfma_flops", "upk_mfma_launch", "upk_mfma16_launch",
+                 "upk_copy_launch"):
         assert hasattr(lib, name), name
     lib.upk_mfma_flops.restype = ctypes.c_double
     lib.upk_mfma_flops.argtypes = [ctypes.c_int32]
@@ -222,6 +223,9 @@ def test_peaks_library_exports_and_rejects():
                                     ctypes.c_void_p]
     assert lib.upk_mfma_launch(None, 4, None) == -1
     assert lib.upk_mfma_launch(FAKE, 0, None) == -1
+    lib.upk_mfma16_launch.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    assert lib.upk_mfma16_launch(None, 4, None) == -1
+    assert lib.upk_mfma16_launch(FAKE, 0, None) == -1
     assert lib.upk_copy_launch(FAKE, FAKE, 100, 4, None) == -1      # not a multiple of 16
     assert lib.upk_copy_launch(FAKE_MIS, FAKE, 64, 4, None) == -1
     assert lib.upk_copy_launch(None, FAKE, 64, 4, None) == -1

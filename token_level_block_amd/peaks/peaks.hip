@@ -9,6 +9,10 @@
 //                    values in [0.5, 2) with random signs are used.  Two
 //                    independent accumulator chains per wave, two waves per
 //                    SIMD (the score kernel's occupancy).
+//   upk_mfma16_launch  the same with v_mfma_f32_16x16x32_bf16 (the FFN
+//                    GEMM's instruction), eight accumulator chains per wave.
+//                    It moves half the accumulator bytes per flop and holds a
+//                    higher clock under the same power limit.
 //   upk_copy_launch  a streaming device copy: one 16-byte nontemporal unit
 //                    per thread, consecutive workgroups on consecutive units
 //                    (the row copies' access pattern without the gather), by
@@ -24,6 +28,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaThreads = 512;   // 8 waves: two per SIMD
@@ -74,6 +79,34 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_peak_kernel(float* out) {
   out[t] = s;
 }
 
+__global__ __launch_bounds__(kMfmaThreads) void mfma16_peak_kernel(float* out) {
+  const uint32_t t = blockIdx.x * kMfmaThreads + threadIdx.x;
+  bf16x8 a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    u32x4 va, vb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      va[e] = random_bf16_pair(t * 97u + i * 13u + e);
+      vb[e] = random_bf16_pair(t * 31u + i * 7u + e + 1000u);
+    }
+    a[i] = __builtin_bit_cast(bf16x8, va);
+    b[i] = __builtin_bit_cast(bf16x8, vb);
+  }
+  floatx4 c[8] = {};
+  for (int it = 0; it < kMfmaSteps; ++it) {
+    // 32 MFMAs of 16x16x32 per trip: the flops of the 32x32x16 loop's 16
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[(i * 2 + j) & 7], b[(i + j) & 7], c[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += (c[j][0] + c[j][1]) + (c[j][2] + c[j][3]);
+  out[t] = s;
+}
+
 // thread t of workgroup w copies units w*256 + t + k*(grid*256), k = 0, 1, ...
 __global__ __launch_bounds__(kCopyThreads) void copy_peak_kernel(const u32x4* __restrict__ src,
                                                                  u32x4* __restrict__ dst, int64_t n) {
@@ -100,6 +133,14 @@ double upk_mfma_flops(int32_t blocks) {
 int32_t upk_mfma_launch(float* out, int32_t blocks, hipStream_t stream) {
   if (out == nullptr || blocks < 1) return -1;
   hipLaunchKernelGGL(mfma_peak_kernel, dim3((unsigned)blocks), dim3(kMfmaThreads), 0, stream, out);
+  return (int32_t)hipGetLastError();
+}
+
+// The 16x16x32 loop: the same flops per launch (upk_mfma_flops), the same
+// output size, the same return values.
+int32_t upk_mfma16_launch(float* out, int32_t blocks, hipStream_t stream) {
+  if (out == nullptr || blocks < 1) return -1;
+  hipLaunchKernelGGL(mfma16_peak_kernel, dim3((unsigned)blocks), dim3(kMfmaThreads), 0, stream, out);
   return (int32_t)hipGetLastError();
 }
 
