@@ -244,6 +244,52 @@ def time_ffn(keep_mask, cu_d, R, T, kept, wl, stream, ev, reps=3):
             "gemms": "ffn_gemm_kernel: bf16 MFMA 16x16x32, fp32 accumulate; SwiGLU fused into the gate/up epilogue"}
 
 
+def vendor_ffn(rows, reps=3):
+    """Context for the FFN GEMM: torch's bf16 F.linear (the vendor GEMM library)
+    on the same products, 131072 rows of LLaMA-3.1-8B widths and the same
+    seeded tensors as the ffn_eq7 record.  The gate/up product is written
+    whole ([rows, 2F], no SwiGLU); the down product reads the h that the
+    library's own gate/up launch leaves in its workspace.  The library's two
+    launches run first on the same tensors, so a kernel trace of this mode
+    holds both side by side.  Not part of the default run."""
+    import torch
+    import torch.nn.functional as Fn
+    import synth
+    import token_level_block_amd as tlb
+    D = 4096
+    F = synth.FFN_INTERMEDIATE["llama8b"]
+    wg, wd = synth.ffn_weights_torch(D, F, "cuda")
+    x = synth.ffn_activations_torch(rows, D, "cuda")
+    y = torch.empty_like(x)
+    ffn = tlb.FFN(D, F)
+    ws = torch.empty(ffn.workspace_bytes(rows), dtype=torch.uint8, device="cuda")
+    h = ws[: rows * F * 2].view(torch.bfloat16).view(rows, F)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def mean_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        marks = [(ev(), ev()) for _ in range(reps)]
+        for a, b in marks:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in marks) / reps
+
+    ours = mean_ms(lambda: ffn.forward(x, rows, wg, wd, y, ws))
+    gu = mean_ms(lambda: Fn.linear(x, wg))
+    dn = mean_ms(lambda: Fn.linear(h, wd))
+    ffn.close()
+    fl = lambda n_out, k: 2.0 * rows * n_out * k
+    return {"rows": rows, "hidden": D, "intermediate": F,
+            "library_ffn_ms": ours, "library_ffn_tflops": 6.0 * rows * D * F / (ours * 1e-3) / 1e12,
+            "vendor_gate_up_ms": gu, "vendor_gate_up_tflops": fl(2 * F, D) / (gu * 1e-3) / 1e12,
+            "vendor_down_ms": dn, "vendor_down_tflops": fl(D, F) / (dn * 1e-3) / 1e12,
+            "note": "vendor gate/up writes the [rows, 2F] product without SwiGLU; per-kernel times "
+                    "come from a kernel trace of this mode"}
+
+
 def ratio(a, b):
     return None if b is None else a / b
 
@@ -635,6 +681,9 @@ def main():
                          "off by default so that a kernel trace of the default run holds only serial launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
+    ap.add_argument("--vendor-ffn", action="store_true",
+                    help="only time the FFN on 131072 rows beside torch's bf16 F.linear on the same products "
+                         "(context for the FFN GEMM; prints one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures the single-GPU hot path only; --gpus {args.gpus} is not supported "
@@ -660,6 +709,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"[bench] copied {src.numel() * 4} bytes three times")
+        return
+
+    if args.vendor_ffn:
+        print(json.dumps(vendor_ffn(131072)), flush=True)
         return
 
     stream = torch.cuda.current_stream().cuda_stream
