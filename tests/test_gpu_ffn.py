@@ -108,6 +108,26 @@ def test_ffn_small_shapes_all_rows(rows, D, F):
     check_rows(y, x, wg, wd, f"{rows}x{D}x{F}")
 
 
+# The tile walk's XCD grids over several groups of 8 token panels (11 panels:
+# a full group and a partial one): 8 and 16 weight panels in both launches
+# (grids of 2 x 4 and 4 x 2 XCDs), and 32 gate/up panels (8 x 1) beside a down
+# launch of 4 (fewer than 8: the plain walk).  One row of every token panel,
+# every output column: each row
+# reads h over all gate/up panels and writes y over all down panels, so every
+# tile of both launches is checked.
+@pytest.mark.parametrize("D,F", [(2048, 1024), (4096, 2048), (1024, 4096)])
+def test_ffn_tile_walk_grids(D, F):
+    rows = 2600
+    wg = synth.uniform_bf16_bits(61 + D, 0, 2 * F, D, -5)
+    wd = synth.uniform_bf16_bits(62 + F, 0, D, F, -5)
+    x = synth.uniform_bf16_bits(63, 0, rows, D, 0)
+    ffn = tlb.FFN(D, F)
+    y = gpu_ffn(ffn, bits_dev(x), rows, bits_dev(wg), bits_dev(wd))
+    pick = np.array(sorted({min(rows - 1, 256 * t + (37 * t) % 256) for t in range((rows + 255) // 256)}
+                           | {rows - 1}))
+    check_rows(y[torch.from_numpy(pick).cuda()], x[pick], wg, wd, f"walk {rows}x{D}x{F}, rows {pick.tolist()}")
+
+
 def test_ffn_zero_rows_is_a_no_op():
     ffn = tlb.FFN(64, 64)
     y = torch.full((4, 64), 3.0, dtype=torch.bfloat16, device="cuda")
