@@ -20,7 +20,7 @@
 // clock about 12 % higher.  Operands stream through LDS with gfx950's direct
 // global-to-LDS 16-byte loads in stages of 64 K-elements: a row's 128 bytes
 // per stage make whole 128-byte L2 requests (64-byte rows took twice the
-// requests, and the L1-to-L2 path is what bounds the kernel).  The 160 KB of
+// requests, and were slower).  The 160 KB of
 // LDS hold a ring of five operand units (one operand's 256 rows of a stage,
 // 32 KB each), so the loads of a unit are issued one to two stages before it
 // is read, spread between the MFMAs (a burst stalls the waves at the texture
