@@ -94,3 +94,42 @@ def test_step_graph_replays_match_eager():
             assert torch.equal(got, want), (i, name)
         for got, want in zip((mb_graph.seq_lens, mb_graph.num_actual_tokens, mb_graph.seqused_base), ref_meta):
             assert torch.equal(got, want), i
+
+
+def test_ffn_graph_replays_match_eager():
+    """The FFN sublayer (its two GEMM launches) captured in a HIP graph: every
+    replay, with eager FFN calls on other inputs in between, reproduces the
+    eager output bit for bit."""
+    rows, D, F = 700, 512, 1536
+    wg = synth.uniform_bf16_bits(71, 0, 2 * F, D, -5)
+    wd = synth.uniform_bf16_bits(72, 0, D, F, -5)
+    to_dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    x = to_dev(synth.uniform_bf16_bits(73, 0, rows, D, 0))
+    x_other = to_dev(synth.uniform_bf16_bits(74, 0, rows, D, 0))
+    wgd, wdd = to_dev(wg), to_dev(wd)
+    ffn = tlb.FFN(D, F)
+    ws = torch.empty(ffn.workspace_bytes(rows), dtype=torch.uint8, device="cuda")
+    y = torch.empty((rows, D), dtype=torch.bfloat16, device="cuda")
+    y_other = torch.empty_like(y)
+    ffn.forward(x, rows, wgd, wdd, y, ws)
+    torch.cuda.synchronize()
+    ref = y.clone()
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ffn.forward(x, rows, wgd, wdd, y, ws, stream=side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        ffn.forward(x, rows, wgd, wdd, y, ws, stream=torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for i in range(4):
+        ffn.forward(x_other, rows, wgd, wdd, y_other, ws)   # eager work on the same workspace
+        y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), i
+    ffn.close()
