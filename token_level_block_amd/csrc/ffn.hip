@@ -299,15 +299,16 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   };
 
   // Iteration st computes stage st, K-step by K-step: 32 MFMAs with the reads
-  // of the next K-step's fragments spread between them; before the last K-step (whose reads are those of stage st + 1's first
-  // K-step) the wave waits for stage st + 1 at a barrier.  Every read of a
-  // stage's units is issued before that barrier and has completed at it
-  // (lgkmcnt(0)).
+  // of the next K-step's fragments spread between them; before the last
+  // K-step (whose reads are those of stage st + 1's first K-step) the wave
+  // waits for stage st + 1 at a barrier.  Every read of a stage's units is
+  // issued before that barrier and has completed at it (lgkmcnt(0)).
   // Steady state (all units involved full): iteration st issues positions
   // kN1 .. 2 kChunks - 1 of sequence st - 1 in K-step 0 and positions
   // 0 .. kN1 - 1 of sequence st after its barrier, in K-step 1.  At the
-  // barrier, stage st + 1's tokens are positions 0 .. kChunks - 1 of sequence
-  // st - 1, and the kChunks loads issued after them may still be in flight.
+  // barrier, stage st + 1's odd unit is positions 0 .. kChunks - 1 of
+  // sequence st - 1, and the kChunks loads issued after them may still be in
+  // flight.
   // Past the steady state, units are issued whole at the top of the iteration
   // (the last stage possibly partial), up to unit 2 st + 4, whose buffer was
   // freed at the barrier before.
