@@ -356,6 +356,21 @@ def test_copy_planner_invariants(tmp_path):
     assert p.stdout.startswith("ok ") and int(p.stdout.split()[1]) > 1000000
 
 
+def test_ffn_tile_walk_covers_every_tile_once(tmp_path):
+    """ffn_walk.h (host C++, the same functions the FFN GEMM kernel calls):
+    for every panel count up to 72 x 70 and the model shapes, the launch's
+    workgroups compute each 256 x 256 tile exactly once, and the first 32
+    workgroups of an XCD share at least 4 weight panels and one group of
+    token panels (tests/ffn_walk_check.cc)."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no C++ compiler")
+    exe = build_host_check(gxx, "ffn_walk_check.cc", tmp_path)
+    p = subprocess.run([exe], capture_output=True, text=True)
+    assert p.returncode == 0, p.stderr
+    assert p.stdout.startswith("ok ") and int(p.stdout.split()[1]) > 1000000
+
+
 def test_select_rejects_a_score_grid_beyond_32_bits():
     """A window so long that (key chunks x query slices) would not fit the
     grid's 32-bit x dimension is rejected at planning, not launched short."""

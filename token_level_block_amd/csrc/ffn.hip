@@ -37,9 +37,10 @@
 // register.  Rows past the end are clamped (their results are not stored) and
 // K past the end reads a zero piece.  The tile walk shares token panels
 // across the XCDs (through the MALL) and weight and token panels among the
-// workgroups of an XCD (through its L2).
+// workgroups of an XCD (through its L2): ffn_walk.h.
 #include "../../include/uniprefill.h"
 #include "common.h"
+#include "ffn_walk.h"
 
 namespace up {
 
@@ -71,7 +72,6 @@ static_assert(kWaves == 8 && kNK == 2, "wave layout and K-step schedule");
 // 256-byte window of banks get distinct pieces
 constexpr int kSwzShift = 1;
 static_assert(kTileI == 256 && kTileJ == 256 && kUnits * kUnitBytes <= 160 * 1024, "LDS");
-constexpr int kGroupJ = 8;                // token panels walked together
 
 __device__ __attribute__((aligned(16))) const uint32_t kZeroPiece[4] = {0u, 0u, 0u, 0u};
 
@@ -109,11 +109,6 @@ constexpr int kRawBufferFlags = 0x00020000;
 // host-side launch stub)
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-// rows of the XCD grid of the tile walk (8, 4 or 2) for tiles_i >= 8 weight panels
-__host__ __device__ constexpr uint32_t ffn_xcd_rows(uint32_t tiles_i) {
-  return tiles_i >= 32 ? 8u : (tiles_i >= 16 ? 4u : 2u);
-}
-
 template <bool kGateUp>
 __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kUnits * kUnitBytes];
@@ -122,44 +117,9 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
   const int wi = wid / (kWaves / 2), wj = wid % (kWaves / 2);
   const int quad = lane >> 4;
 
-  // tile of this workgroup.  Workgroups are dealt to the 8 XCDs round-robin
-  // (XCD x = id mod 8 runs the ones with id / 8 = 0, 1, 2, ... in turn).
-  // With 8 or more weight panels the XCDs form an xi x (8 / xi) grid: XCD x
-  // takes the (x mod xi)-th of xi equal runs of weight panels and every
-  // (8 / xi)-th group of kGroupJ token panels, starting at group x / xi, and
-  // walks them group by group.  The 32 workgroups an XCD runs together then
-  // cover at least 4 weight panels times a group of token panels (xi is the
-  // largest of 8, 4, 2 that leaves each XCD 4 weight panels or more), which
-  // they share in its L2; the XCDs of one column walk the same token groups
-  // at once, so a token panel leaves HBM once and their other L2 misses on it
-  // hit the MALL.  Otherwise XCD x walks tiles [x T/8, (x+1) T/8) in order.
-  // (32-bit arithmetic: the host keeps every tile count, and the grid, below 2^32)
-  int ti, tj;
-  {
-    const uint32_t x = blockIdx.x & 7;
-    const uint32_t q = blockIdx.x >> 3;
-    const uint32_t tiles_i = (uint32_t)a.tiles_i, tiles_j = (uint32_t)a.tiles_j;
-    uint32_t wgi, grp, ti0;
-    if (tiles_i >= 8) {
-      const uint32_t xi = ffn_xcd_rows(tiles_i), xj = 8 / xi;
-      const uint32_t gi = x % xi;
-      ti0 = gi * tiles_i / xi;
-      const uint32_t nti = (gi + 1) * tiles_i / xi - ti0;
-      grp = (q / (nti * kGroupJ)) * xj + x / xi;
-      wgi = q % (nti * kGroupJ);
-      if (grp * kGroupJ >= tiles_j || wgi >= nti * min((uint32_t)kGroupJ, tiles_j - grp * kGroupJ)) return;
-    } else {
-      const uint32_t ntiles = tiles_i * tiles_j;
-      const uint32_t t = x * ((ntiles + 7) / 8) + q;
-      if (t >= ntiles) return;
-      ti0 = 0;
-      grp = t / (kGroupJ * tiles_i);
-      wgi = t % (kGroupJ * tiles_i);
-    }
-    const uint32_t gj = min((uint32_t)kGroupJ, tiles_j - grp * kGroupJ);
-    ti = (int)(ti0 + wgi / gj);
-    tj = (int)(grp * kGroupJ + wgi % gj);
-  }
+  // tile of this workgroup (ffn_walk.h)
+  int ti = 0, tj = 0;
+  if (!ffn_tile_of(blockIdx.x & 7, blockIdx.x >> 3, (uint32_t)a.tiles_i, (uint32_t)a.tiles_j, &ti, &tj)) return;
 
   const int64_t K = a.K;
   const int64_t n_w = kGateUp ? 2 * a.F : a.n_out;   // weight rows
@@ -439,15 +399,6 @@ __global__ __launch_bounds__(kFfnThreads, 1) void ffn_gemm_kernel(FfnGemmArgs a)
     const int64_t col = col0 + p * 8;
     if (j < a.rows && col < ncols) *reinterpret_cast<u32x4*>(a.out + j * a.n_out + col) = v;
   }
-}
-
-// workgroups the kernel's tile walk takes: 8 times the most tiles any XCD
-// can get (ids past an XCD's share exit at once)
-int64_t ffn_gemm_grid(int64_t tiles_i, int64_t tiles_j) {
-  if (tiles_i < 8) return (tiles_i * tiles_j + 7) / 8 * 8;
-  const int64_t xi = ffn_xcd_rows((uint32_t)(tiles_i < 32 ? tiles_i : 32)), xj = 8 / xi;
-  const int64_t groups = (tiles_j + kGroupJ - 1) / kGroupJ;
-  return 8 * ((tiles_i + xi - 1) / xi) * kGroupJ * ((groups + xj - 1) / xj);
 }
 
 static hipError_t launch_ffn_gemm(bool gate_up, const FfnGemmArgs& a, hipStream_t s) {
